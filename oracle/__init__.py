@@ -1,0 +1,48 @@
+"""CPU oracle for the online-softmax row kernel and the fused attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
+anything in this package: it is used by ``tests/``, by ``__graft_entry__.smoke()``
+and by the ``cpu_baseline`` leg of ``bench.py``, and by nothing else.
+
+Every function here is a plain, slow, float64 restatement of the definitions on
+the source pages:
+
+* "Ch.6 Softmax and Online Softmax" (yangyitao.com, the CUDA FlashAttention-v2
+  book), cited below as [Ch6 §x];
+* the xxqk.cn article on parallelising softmax, Online Softmax and
+  FlashAttention, cited as [xxqk §x];
+* the mooersco.com article "FlashAttention 2.0 in LLM inference", cited as
+  [mooers §x].
+
+Modules
+-------
+softmax_ref    three-pass safe softmax ([Ch6 §6.2]) and the unsafe two-pass
+               form ([Ch6 §6.1]) kept as a negative control.
+online_ref     the element-wise online normaliser and the (m, l) combine
+               ([Ch6 §6.3.1], [Ch6 §6.4.1]); used only to check the oracle
+               itself (online == two-pass by brute force).
+attention_ref  materialised-S attention with log-sum-exp ([Ch6 §6.5],
+               [Ch6 §6.6], [xxqk §4.2]) and the single-query blocked alpha/beta
+               form ([Ch6 §6.6]) as a self-check.
+
+The oracle shares no code with the HIP library and never imports it.  Pins that
+tie it to something other than itself live in ``tests/test_oracle_*.py``.
+Parity status of each function is stated in its docstring.
+"""
+
+from .softmax_ref import softmax_rows_ref, naive_softmax_rows_f32
+from .online_ref import EMPTY_STATE, all_trees, combine, online_state, tree_reduce
+from .attention_ref import attention_head_ref, attention_ref, blocked_attention_row_ref
+
+__all__ = [
+    "softmax_rows_ref",
+    "naive_softmax_rows_f32",
+    "EMPTY_STATE",
+    "combine",
+    "online_state",
+    "tree_reduce",
+    "all_trees",
+    "attention_head_ref",
+    "attention_ref",
+    "blocked_attention_row_ref",
+]

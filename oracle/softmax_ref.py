@@ -1,0 +1,83 @@
+"""Row softmax oracle (test infrastructure only; see the package docstring).
+
+Parity status: pinned.  ``softmax_rows_ref`` is checked against the worked
+example of [Ch6 §6.3.2], against torch's CPU softmax in float64, against row-sum
+and shift-invariance identities, and on the overflow / -inf rows the pages
+discuss ([Ch6 §6.2], [Ch6 §6.4]).  The fully -inf row is defined here to give
+all zeros; the chapter notes that torch returns NaN (0/0) for it ([Ch6 §6.7.3]),
+and the library's contract fixes 0 instead.
+"""
+
+import numpy as np
+
+
+def softmax_rows_ref(x, return_stats=False):
+    """Safe softmax of every row of a 2-D array, in float64, three passes.
+
+    Follows [Ch6 §6.2]: subtract the row maximum ``m = max_j x_j``, sum
+    ``exp(x_j - m)``, then divide each ``exp(x_i - m)`` by that sum.  This is the
+    plain definition of [Ch6 §6.1] made overflow-free; it is the result the
+    online recurrence of [Ch6 §6.3] reaches exactly in real arithmetic.
+
+    Entries equal to -inf contribute exp(-inf) = 0.  A row whose entries are all
+    -inf has no finite maximum; its output is all zeros, its sum 0 and its
+    log-sum-exp -inf.  +inf and NaN inputs are outside the contract and simply
+    propagate.
+
+    Parameters
+    ----------
+    x : array_like, shape (rows, cols)
+        Converted to float64 exactly (float32 and bfloat16 values are exactly
+        representable in float64).
+    return_stats : bool
+        Also return the per-row max ``m``, the sum ``s`` and ``lse = m + log s``
+        ([Ch6 §6.5]).
+
+    Returns
+    -------
+    y : ndarray float64, shape (rows, cols)
+    (m, s, lse) : three float64 arrays of shape (rows,), when requested.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim != 2:
+        raise ValueError("softmax_rows_ref expects a 2-D array")
+    rows, cols = x.shape
+    y = np.zeros((rows, cols), dtype=np.float64)
+    m_out = np.full(rows, -np.inf)
+    s_out = np.zeros(rows)
+    for r in range(rows):
+        row = x[r]
+        if cols == 0:
+            continue
+        # Pass 1: the maximum.
+        m = np.max(row)
+        m_out[r] = m
+        if m == -np.inf:
+            # Every entry masked: defined as an all-zero row.
+            continue
+        # Pass 2: the denominator relative to m.
+        e = np.exp(row - m)
+        s = np.sum(e)
+        s_out[r] = s
+        # Pass 3: each output.
+        y[r] = np.exp(row - m) / s
+    if not return_stats:
+        return y
+    with np.errstate(divide="ignore"):
+        lse = np.where(s_out > 0, m_out + np.log(np.where(s_out > 0, s_out, 1.0)), -np.inf)
+    return y, (m_out, s_out, lse)
+
+
+def naive_softmax_rows_f32(x):
+    """The unsafe two-pass softmax of [Ch6 §6.1], evaluated in float32.
+
+    Negative control only: no maximum is subtracted, so rows of values near
+    1000 overflow to inf/inf = NaN exactly as [Ch6 §6.2] describes.  Tests use it
+    to show that the overflow rows really exercise the overflow they are meant
+    to.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.exp(x)
+        s = np.sum(e, axis=1, keepdims=True, dtype=np.float32)
+        return e / s
