@@ -1,0 +1,117 @@
+/*
+ * osm.h -- C ABI of libosm: online softmax and the fused attention forward
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (cited by page title and section):
+ *   [Ch6]   "Ch.6 Softmax and Online Softmax", yangyitao.com CUDA
+ *           FlashAttention-v2 book.
+ *   [xxqk]  m.xxqk.cn article on parallelising softmax, Online Softmax and
+ *           FlashAttention.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE memory owned by the caller.  The library
+ *     allocates nothing, frees nothing and keeps no state between calls; calls
+ *     from several host threads are safe.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ *     the call returns without waiting.  The caller synchronises.
+ *   - Arguments are validated on the host before any HIP call.  An invalid call
+ *     returns OSM_ERR_INVALID_ARG or OSM_ERR_UNSUPPORTED and launches nothing.
+ *     A launch failure reported by the runtime returns OSM_ERR_HIP.  Nothing is
+ *     printed and nothing aborts.
+ *   - Results are deterministic: reductions use a fixed order and no atomics,
+ *     so the same inputs give bitwise-identical outputs on the same device.
+ */
+#ifndef OSM_H_
+#define OSM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OSM_F32 = 0,  /* IEEE binary32 */
+  OSM_BF16 = 1  /* bfloat16 (8-bit exponent, 7-bit stored mantissa) */
+} osm_dtype;
+
+typedef enum {
+  OSM_OK = 0,
+  OSM_ERR_INVALID_ARG = 1,  /* null pointer, negative size, unknown dtype, overflow */
+  OSM_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+  OSM_ERR_HIP = 3           /* the HIP runtime reported an error at launch */
+} osm_status;
+
+/*
+ * osm_softmax_rows -- row-wise softmax of a row-major [rows, cols] matrix.
+ *
+ * Computes out[r, i] = exp(in[r, i] - m_r) / sum_j exp(in[r, j] - m_r) with
+ * m_r the row maximum: the safe softmax of [Ch6 §6.2], evaluated with the
+ * online normaliser of [Ch6 §6.3.1] (a running max m and a rescaled sum l per
+ * lane) and the associative (m, l) combine of [Ch6 §6.4.1] across lanes and
+ * wavefronts.  Each row is read from HBM once and written once.
+ *
+ *   in, out  device pointers to contiguous row-major [rows, cols] arrays of
+ *            `dtype` (no row stride).  in == out (in place) is allowed; any
+ *            other overlap is not.  Element alignment is required; 16-byte
+ *            alignment with cols a multiple of 16 bytes takes the vector path.
+ *   rows     number of rows, >= 0.
+ *   cols     row length, >= 0 and < 2^31.  rows == 0 or cols == 0 is a
+ *            successful no-op (pointers may then be NULL).
+ *   dtype    OSM_F32 or OSM_BF16; input and output share it.  Arithmetic is
+ *            float32; bfloat16 outputs are rounded to nearest even.
+ *   stream   hipStream_t to enqueue on.
+ *
+ * Values: -inf entries contribute 0 and produce 0.  A row whose entries are
+ * all -inf produces all zeros (where an unguarded 0/0 would give NaN,
+ * [Ch6 §6.7.3]).  +inf and NaN inputs are outside the contract.
+ *
+ * Returns OSM_OK, or OSM_ERR_INVALID_ARG (null pointer with nonzero size,
+ * negative or too large size, unknown dtype, misaligned pointer), or
+ * OSM_ERR_HIP.
+ */
+int osm_softmax_rows(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                     void* stream);
+
+/*
+ * osm_attn_fwd -- fused attention forward with per-row log-sum-exp.
+ *
+ * For every batch b, head h and query row i:
+ *   S[i, j] = scale * dot(q[b,h,i,:], k[b,h,j,:])            ([xxqk §4.1])
+ *   with causal != 0, S[i, j] = -inf for j > i              ([xxqk §6.3])
+ *   o[b,h,i,:] = sum_j softmax_j(S[i, :]) * v[b,h,j,:]
+ *   lse[b,h,i] = log sum_j exp(S[i, j])                     ([Ch6 §6.5])
+ * The scores are never written to memory: key/value tiles stream through
+ * on-chip memory and the running (m, l) and the output accumulator are
+ * rescaled per tile ([Ch6 §6.6], [xxqk §4.1]); the division by l happens once
+ * at the end.
+ *
+ *   q, k, v  device pointers, contiguous [B, H, N, D] bfloat16.
+ *   o        device pointer, contiguous [B, H, N, D] bfloat16 (rounded to
+ *            nearest even).  Must not overlap q, k, v or lse.
+ *   lse      device pointer, contiguous [B, H, N] float32: natural log of the
+ *            sum of exp over the scaled, unmasked scores (-inf if none).
+ *   B, H, N  >= 0; any N (tails are masked).  B*H*N == 0 is a no-op.
+ *   D        head dimension: 64 or 128 (others return OSM_ERR_UNSUPPORTED).
+ *   scale    multiplier applied to q.k (e.g. 1/sqrt(D)); finite and > 0.
+ *   causal   0: every key visible; nonzero: key j visible to query i iff j <= i.
+ *   stream   hipStream_t to enqueue on.
+ *
+ * Returns OSM_OK, OSM_ERR_INVALID_ARG (null pointer with nonzero size, negative
+ * size, B*H*N*D overflowing int64, non-finite or non-positive scale, pointer
+ * not 16-byte aligned), OSM_ERR_UNSUPPORTED (D not 64 or 128), or OSM_ERR_HIP.
+ */
+int osm_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int H, int N, int D, float scale, int causal, void* stream);
+
+/* Human-readable name of a status code; never NULL, static storage. */
+const char* osm_status_string(int status);
+
+/* Library version as "major.minor.patch"; static storage. */
+const char* osm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSM_H_ */

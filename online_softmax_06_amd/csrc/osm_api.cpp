@@ -1,0 +1,70 @@
+// C ABI of libosm (declared in include/osm.h): host-side validation and
+// dispatch.  No HIP call is made before the arguments have been checked, so
+// invalid calls return a status without touching the device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "osm.h"
+#include "osm_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? OSM_OK : OSM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* osm_status_string(int status) {
+  switch (status) {
+    case OSM_OK: return "OSM_OK";
+    case OSM_ERR_INVALID_ARG: return "OSM_ERR_INVALID_ARG: invalid argument";
+    case OSM_ERR_UNSUPPORTED: return "OSM_ERR_UNSUPPORTED: unsupported configuration";
+    case OSM_ERR_HIP: return "OSM_ERR_HIP: HIP runtime error at launch";
+    default: return "OSM_ERR_UNKNOWN: unknown status code";
+  }
+}
+
+const char* osm_version(void) { return "0.1.0"; }
+
+int osm_softmax_rows(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                     void* stream) {
+  if (dtype != OSM_F32 && dtype != OSM_BF16) return OSM_ERR_INVALID_ARG;
+  if (rows < 0 || cols < 0 || cols > INT32_MAX) return OSM_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return OSM_OK;
+  if (in == nullptr || out == nullptr) return OSM_ERR_INVALID_ARG;
+  const int64_t esize = dtype == OSM_F32 ? 4 : 2;
+  if (rows > INT64_MAX / cols / esize) return OSM_ERR_INVALID_ARG;
+  if (!aligned(in, esize) || !aligned(out, esize)) return OSM_ERR_INVALID_ARG;
+  const int64_t vec = 16 / esize;
+  const bool vector_path = aligned(in, 16) && aligned(out, 16) && (cols % vec) == 0;
+  return from_hip(osm::softmax_rows_launch(in, out, rows, (int)cols, dtype, vector_path,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int osm_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int D, float scale, int causal, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || D < 0) return OSM_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return OSM_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return OSM_ERR_UNSUPPORTED;
+  const int64_t bh = (int64_t)B * (int64_t)H;  // < 2^62: no overflow
+  if (bh > INT32_MAX) return OSM_ERR_INVALID_ARG;
+  const int64_t bhn = bh * (int64_t)N;         // < 2^62: no overflow
+  if (bhn == 0) return OSM_OK;
+  if (bhn > INT64_MAX / (2 * (int64_t)D)) return OSM_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !lse) return OSM_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return OSM_ERR_INVALID_ARG;
+  // One 256-thread workgroup per 128 query rows of each (batch, head): the
+  // launch must stay below 2^32 work-items.
+  const int64_t workgroups = bh * (((int64_t)N + 127) / 128);
+  if (workgroups * 256 >= ((int64_t)1 << 32)) return OSM_ERR_UNSUPPORTED;
+  return from_hip(osm::attn_fwd_launch(q, k, v, o, lse, B, H, N, D, scale, causal != 0,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU.
+
+The library must load, export every function include/osm.h declares, and
+reject invalid arguments with a status code before making any HIP call (so the
+calls below are safe on a machine without a GPU: none of them launches).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import online_softmax_06_amd as osm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "osm.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(osm_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(osm.lib_path()):
+        pytest.fail("libosm.so is not built: run `python -m online_softmax_06_amd.build`")
+    return osm.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == ["osm_attn_fwd", "osm_softmax_rows", "osm_status_string",
+                                     "osm_version"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(osm.lib_path())
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_python_layer_exposes_the_same_names():
+    for name in _declared_functions():
+        assert callable(getattr(osm, name)), name
+
+
+def test_status_strings(lib):
+    assert osm.osm_status_string(osm.OSM_OK) == "OSM_OK"
+    for st in (osm.OSM_ERR_INVALID_ARG, osm.OSM_ERR_UNSUPPORTED, osm.OSM_ERR_HIP):
+        assert osm.osm_status_string(st).startswith("OSM_ERR_")
+    assert "UNKNOWN" in osm.osm_status_string(12345)
+    assert re.match(r"^\d+\.\d+\.\d+$", osm.osm_version())
+
+
+FAKE = 0x10000  # 64 KiB-aligned fake device address; never dereferenced
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((FAKE, FAKE, -1, 10, 0), osm.OSM_ERR_INVALID_ARG),        # negative rows
+    ((FAKE, FAKE, 10, -1, 0), osm.OSM_ERR_INVALID_ARG),        # negative cols
+    ((FAKE, FAKE, 10, 10, 2), osm.OSM_ERR_INVALID_ARG),        # unknown dtype
+    ((FAKE, FAKE, 10, 10, -1), osm.OSM_ERR_INVALID_ARG),       # unknown dtype
+    ((0, FAKE, 10, 10, 0), osm.OSM_ERR_INVALID_ARG),           # null input
+    ((FAKE, 0, 10, 10, 1), osm.OSM_ERR_INVALID_ARG),           # null output
+    ((FAKE + 2, FAKE, 10, 10, 0), osm.OSM_ERR_INVALID_ARG),    # fp32 misaligned
+    ((FAKE + 1, FAKE, 10, 10, 1), osm.OSM_ERR_INVALID_ARG),    # bf16 misaligned
+    ((FAKE, FAKE, 10, 2 ** 31, 0), osm.OSM_ERR_INVALID_ARG),   # cols too large
+    ((FAKE, FAKE, 2 ** 62, 2 ** 20, 0), osm.OSM_ERR_INVALID_ARG),  # size overflow
+    ((0, 0, 0, 10, 0), osm.OSM_OK),                            # empty: no-op
+    ((0, 0, 10, 0, 1), osm.OSM_OK),                            # empty: no-op
+])
+def test_softmax_argument_checks(lib, args, expect):
+    assert osm.osm_softmax_rows(*args, 0) == expect
+
+
+def _attn(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, D=64, scale=0.125, causal=0):
+    return osm.osm_attn_fwd(q, k, v, o, lse, B, H, N, D, scale, causal, 0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(D=96), osm.OSM_ERR_UNSUPPORTED),
+    (dict(D=32), osm.OSM_ERR_UNSUPPORTED),
+    (dict(D=256), osm.OSM_ERR_UNSUPPORTED),
+    (dict(B=-1), osm.OSM_ERR_INVALID_ARG),
+    (dict(N=-5), osm.OSM_ERR_INVALID_ARG),
+    (dict(scale=0.0), osm.OSM_ERR_INVALID_ARG),
+    (dict(scale=-0.1), osm.OSM_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), osm.OSM_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), osm.OSM_ERR_INVALID_ARG),
+    (dict(q=0), osm.OSM_ERR_INVALID_ARG),
+    (dict(lse=0), osm.OSM_ERR_INVALID_ARG),
+    (dict(o=FAKE + 8), osm.OSM_ERR_INVALID_ARG),
+    (dict(B=2 ** 30, H=2 ** 30, N=2 ** 30), osm.OSM_ERR_INVALID_ARG),
+    (dict(N=0, q=0, k=0, v=0, o=0, lse=0), osm.OSM_OK),
+    (dict(B=0), osm.OSM_OK),
+])
+def test_attention_argument_checks(lib, kw, expect):
+    assert _attn(**kw) == expect
+
+
+def test_tensor_helpers_reject_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        osm.softmax_rows(torch.zeros(2, 3))
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        osm.attn_fwd(x, x, x)

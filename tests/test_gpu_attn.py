@@ -1,0 +1,139 @@
+"""GPU parity tests of osm_attn_fwd against the float64 CPU oracle.
+
+Tolerances: bfloat16 O, max |gpu - oracle| <= 2e-2; float32 LSE,
+max |gpu - oracle| <= 1e-3.  Small shapes are compared in full; the large
+workloads on seeded (b, h) slices, every query row of each slice, in the same
+launch configuration the benchmark times.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_06_amd as osm
+import osm_inputs
+from oracle import attention_ref
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    osm.load_library()
+
+
+def _announce(*what):
+    print("[case]", *what, flush=True)
+
+
+def compare(q, k, v, scale, causal, o, lse, heads=None):
+    """Oracle on the host copies of q, k, v; returns (max O err, max LSE err)."""
+    qh, kh, vh = (t.cpu().double().numpy() for t in (q, k, v))
+    O, L = attention_ref(qh, kh, vh, scale, causal, heads=heads)
+    og = o.cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    if heads is not None:
+        og = np.stack([og[b, h] for b, h in heads])
+        lg = np.stack([lg[b, h] for b, h in heads])
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    eo = np.abs(og - O).max()
+    el = np.abs(lg - L).max()
+    assert eo <= O_TOL, f"O max abs err {eo}"
+    assert el <= LSE_TOL, f"LSE max abs err {el}"
+    return eo, el
+
+
+def test_small_config_full():
+    cfg = osm_inputs.attention_config("attn_small")
+    _announce("attn_small", cfg["cfg"])
+    q, k, v = (t.cuda() for t in (cfg["q"], cfg["k"], cfg["v"]))
+    o, lse = osm.attn_fwd(q, k, v, cfg["scale"], cfg["causal"])
+    torch.cuda.synchronize()
+    eo, el = compare(q, k, v, cfg["scale"], cfg["causal"], o, lse)
+    print(f"[result] attn_small O err {eo:.3g} LSE err {el:.3g}", flush=True)
+
+
+ODD = [
+    (1, 1, 1, 64), (1, 2, 17, 64), (2, 1, 64, 64), (1, 3, 100, 64), (1, 1, 129, 64),
+    (1, 2, 255, 64), (1, 1, 1000, 64),
+    (1, 1, 1, 128), (1, 2, 17, 128), (2, 1, 64, 128), (1, 3, 100, 128), (1, 1, 129, 128),
+    (1, 2, 255, 128), (1, 1, 1000, 128), (1, 1, 2049, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,D", ODD)
+def test_odd_shapes_full(B, H, N, D, causal):
+    _announce("odd", B, H, N, D, causal)
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=B * 1000 + H * 100 + N + D,
+                                          device="cuda")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = osm.attn_fwd(q, k, v, scale, causal)
+    torch.cuda.synchronize()
+    compare(q, k, v, scale, causal, o, lse)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_closed_forms(D):
+    _announce("closed forms", D)
+    B, H, N = 1, 2, 200
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=77, device="cuda")
+    # Causal row 0 sees only key 0: O = v_0, LSE = scale * q_0 . k_0.
+    o, lse = osm.attn_fwd(q, k, v, 0.1, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
+    s0 = 0.1 * (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1)
+    assert (lse[:, :, 0].double() - s0).abs().max() < 1e-4
+    # Identical keys: uniform weights over the visible keys.
+    kk = k[:, :, :1].expand(B, H, N, D).contiguous()
+    o, lse = osm.attn_fwd(q, kk, v, 0.1, True)
+    torch.cuda.synchronize()
+    cnt = torch.arange(1, N + 1, device="cuda", dtype=torch.float64)
+    mean = v.double().cumsum(2) / cnt[None, None, :, None]
+    assert (o.double() - mean).abs().max() < O_TOL
+    want = 0.1 * (q.double() * kk.double()).sum(-1) + torch.log(cnt)
+    assert (lse.double() - want).abs().max() < LSE_TOL
+
+
+def test_deterministic_and_no_overrun():
+    _announce("determinism/guard")
+    B, H, N, D = 2, 3, 300, 128
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=5, device="cuda")
+    pad = 8192
+    obuf = torch.full((B * H * N * D + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((B * H * N + 2 * pad,), 7.0, dtype=torch.float32, device="cuda")
+    o = obuf[pad:pad + B * H * N * D].view(B, H, N, D)
+    lse = lbuf[pad:pad + B * H * N].view(B, H, N)
+    osm.attn_fwd(q, k, v, 0.088, True, out=o, lse=lse)
+    o1, l1 = o.clone(), lse.clone()
+    osm.attn_fwd(q, k, v, 0.088, True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o1) and torch.equal(lse, l1)
+    assert (obuf[:pad] == 7).all() and (obuf[pad + o.numel():] == 7).all()
+    assert (lbuf[:pad] == 7).all() and (lbuf[pad + lse.numel():] == 7).all()
+
+
+@pytest.mark.parametrize("name,count,must", [
+    ("attn_llama13b", 8, [(0, 0), (7, 39)]),
+    ("attn_long", 4, [(0, 0), (0, 31)]),
+])
+def test_large_configs_sampled_heads(name, count, must):
+    cfg = osm_inputs.attention_config(name, device="cuda")
+    c = cfg["cfg"]
+    _announce(name, c)
+    o, lse = osm.attn_fwd(cfg["q"], cfg["k"], cfg["v"], cfg["scale"], cfg["causal"])
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    heads = osm_inputs.sample_heads(c["B"], c["H"], count, c["seed"], must)
+    sel = lambda t: torch.stack([t[b, h] for b, h in heads])[:, None]  # noqa: E731
+    qs, ks, vs = sel(cfg["q"]), sel(cfg["k"]), sel(cfg["v"])
+    os_, ls = sel(o), torch.stack([lse[b, h] for b, h in heads])[:, None]
+    eo, el = compare(qs, ks, vs, cfg["scale"], cfg["causal"], os_, ls)
+    print(f"[result] {name} heads {heads} O err {eo:.3g} LSE err {el:.3g}", flush=True)
