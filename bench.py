@@ -1,0 +1,285 @@
+"""Benchmark of the online-softmax hot path on one MI355X.
+
+One step is one pass of the whole path over resident synthetic inputs:
+  1. row softmax, float32, 32768 x 8192      (HBM-bound, 1 read + 1 write)
+  2. row softmax, bfloat16, 32768 x 8192     (same, half the bytes)
+  3. fused causal attention forward, bfloat16, B=8 H=40 N=2048 D=128
+     (LLaMA-2-13B-shaped layer; bound by the bf16 matrix cores)
+
+Printed: one JSON line.  ``value`` is the softmax throughput of the
+bandwidth-scale workload (algorithmic bytes of both softmax runs / their
+kernel time); the attention throughput is in ``attention``.  ``rooflines``
+holds each kernel against its roofline; ``roofline`` repeats the kernel that
+takes the largest share of a step.  Kernel times come from HIP events recorded
+on the launch stream around every launch of the timed steps.
+
+``--only`` runs a single unit (for profiler runs); ``--copy`` times a plain
+device copy of the float32 softmax bytes (the counter calibration kernel).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz
+
+METRIC = "softmax GB/s (% HBM peak); attention fwd TFLOPS (% bf16 MFMA peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+SRC_DIR = os.path.join(ROOT, "online_softmax_06_amd", "csrc")
+
+
+def kernel_source_hash(fname):
+    h = hashlib.sha256()
+    for f in (fname, "osm_device.h"):
+        with open(os.path.join(SRC_DIR, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Per-kernel HBM bytes per launch from the committed counter summary.
+
+    Lines look like ``unit=<name> src=<hash> fetch_bytes=<n> write_bytes=<n>``.
+    A unit whose kernel source hash no longer matches gets no figure.
+    """
+    out = {}
+    if not os.path.exists(TRAFFIC_FILE):
+        return out
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            kv = dict(re.findall(r"(\w+)=(\S+)", line))
+            if "unit" in kv and "src" in kv:
+                out[kv["unit"]] = kv
+    return out
+
+
+class Unit:
+    def __init__(self, name, kernel, src, launch, work, bound, peak, unit, workload):
+        self.name, self.kernel, self.src = name, kernel, src
+        self.launch, self.work, self.bound, self.peak = launch, work, bound, peak
+        self.unit, self.workload = unit, workload
+        self.times_ms = []
+
+
+def make_units(torch, osm, osm_inputs, only):
+    units = []
+    c = osm_inputs.SOFTMAX_LARGE
+    for dt, tag in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+        name = f"softmax_{tag}"
+        if only not in (None, name):
+            continue
+        x = osm_inputs.softmax_large(dtype=dt, device="cuda")
+        y = torch.empty_like(x)
+        nbytes = 2 * x.numel() * x.element_size()  # one read + one write per element
+        units.append(Unit(
+            name, f"softmax_resident_kernel ({tag})", "softmax_rows.hip",
+            (lambda x=x, y=y: osm.softmax_rows(x, out=y)), nbytes, "hbm", HBM_PEAK_GBS, "GB/s",
+            f"softmax_large {c['rows']}x{c['cols']} {tag}"))
+    if only in (None, "attn"):
+        cfg = osm_inputs.attention_config("attn_llama13b", device="cuda")
+        a = cfg["cfg"]
+        o = torch.empty_like(cfg["q"])
+        lse = torch.empty((a["B"], a["H"], a["N"]), dtype=torch.float32, device="cuda")
+        # Algorithmic FLOPs: QK^T and PV over the unmasked (query, key) pairs,
+        # 2 * 2 * D per pair; causal pairs = N (N + 1) / 2 per head.
+        pairs = a["N"] * (a["N"] + 1) // 2 if a["causal"] else a["N"] * a["N"]
+        flops = 4 * a["D"] * pairs * a["B"] * a["H"]
+        units.append(Unit(
+            "attn", "attn_fwd_kernel<128, causal>", "attn_fwd.hip",
+            (lambda cfg=cfg, o=o, lse=lse: osm.attn_fwd(cfg["q"], cfg["k"], cfg["v"], cfg["scale"],
+                                                        cfg["causal"], out=o, lse=lse)),
+            flops, "mfma", BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
+            f"attn_llama13b B{a['B']} H{a['H']} N{a['N']} D{a['D']} causal"))
+    return units
+
+
+def cpu_baseline(torch, osm_inputs, budget_s):
+    """Time the float64 oracle on bounded samples of the same workloads."""
+    import numpy as np
+    from oracle import attention_ref, softmax_rows_ref
+    try:
+        import threadpoolctl
+        blas_threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info())
+    except Exception:
+        blas_threads = None
+    c = osm_inputs.SOFTMAX_LARGE
+    x = osm_inputs.softmax_large(device="cuda")
+    rows_done, t_sm = 0, 0.0
+    chunk = 1024
+    while rows_done < c["rows"] and t_sm < budget_s * 0.6:
+        xs = x[rows_done:rows_done + chunk].double().cpu().numpy()
+        t0 = time.perf_counter()
+        softmax_rows_ref(xs)
+        t_sm += time.perf_counter() - t0
+        rows_done += xs.shape[0]
+    del x
+    sm_bytes = 2 * rows_done * c["cols"] * 4
+    cfg = osm_inputs.attention_config("attn_llama13b", device="cuda")
+    a = cfg["cfg"]
+    heads = osm_inputs.sample_heads(a["B"], a["H"], a["B"] * a["H"], a["seed"], [(0, 0)])
+    done, t_at = [], 0.0
+    for (b, h) in heads:
+        if t_at >= budget_s * 0.4:
+            break
+        q, k, v = (cfg[n][b, h][None, None].double().cpu().numpy() for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        attention_ref(q, k, v, cfg["scale"], True)
+        t_at += time.perf_counter() - t0
+        done.append((b, h))
+    at_flops = 4 * a["D"] * (a["N"] * (a["N"] + 1) // 2) * len(done)
+    return {
+        "value": round(sm_bytes / t_sm / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"float64 three-pass softmax oracle (numpy, single-threaded) on the first "
+                   f"{rows_done} of {c['rows']} rows of softmax_large fp32 ({t_sm:.1f} s)"),
+        "attention": {
+            "value": round(at_flops / t_at / 1e12, 6), "unit": "TFLOP/s",
+            "cores": blas_threads, "kind": "oracle",
+            "sample": (f"float64 materialised-score oracle (numpy + BLAS) on {len(done)} of "
+                       f"{a['B'] * a['H']} (b, h) slices of attn_llama13b ({t_at:.1f} s)")},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["softmax_f32", "softmax_bf16", "attn"], default=None)
+    ap.add_argument("--copy", action="store_true", help="time a plain device copy instead")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not "
+              "supported: the kernels shard by (batch, head) or by row with no exchange, and "
+              "this benchmark measures one GPU's share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import online_softmax_06_amd as osm
+    import osm_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    osm.load_library()
+
+    if args.copy:
+        x = osm_inputs.softmax_large(device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(args.warmup):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(args.steps):
+            y.copy_(x)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        print(json.dumps({"copy_bytes": 2 * x.numel() * 4, "ms": ms,
+                          "GB/s": 2 * x.numel() * 4 / ms / 1e6}))
+        return
+
+    units = make_units(torch, osm, osm_inputs, args.only)
+    for _ in range(args.warmup):
+        for u in units:
+            u.launch()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    marks = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in units] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for i, u in enumerate(units):
+            marks[s][i][0].record(stream)
+            u.launch()
+            marks[s][i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    for s in range(args.steps):
+        for i, u in enumerate(units):
+            u.times_ms.append(marks[s][i][0].elapsed_time(marks[s][i][1]))
+
+    traffic = read_traffic()
+    rooflines = []
+    for u in units:
+        avg_ms = sum(u.times_ms) / len(u.times_ms)
+        med_ms = sorted(u.times_ms)[len(u.times_ms) // 2]
+        achieved = u.work / (avg_ms * 1e-3) / (1e9 if u.unit == "GB/s" else 1e12)
+        tr = traffic.get(u.name)
+        tr_bytes = None
+        if tr and tr.get("src") == kernel_source_hash(u.src):
+            tr_bytes = int(float(tr["fetch_bytes"])) + int(float(tr["write_bytes"]))
+        rooflines.append({
+            "unit_name": u.name, "kernel": u.kernel, "workload": u.workload,
+            "bound": u.bound, "achieved": round(achieved, 2), "peak": u.peak, "unit": u.unit,
+            "frac": round(achieved / u.peak, 4), "traffic": tr_bytes,
+            "algorithmic": u.work, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5),
+            "min_ms": round(min(u.times_ms), 5), "max_ms": round(max(u.times_ms), 5)})
+    dominant = max(rooflines, key=lambda r: r["avg_ms"])
+
+    sm = [r for r in rooflines if r["unit_name"].startswith("softmax")]
+    at = [r for r in rooflines if r["unit_name"] == "attn"]
+    if sm:
+        sm_bytes = sum(r["algorithmic"] for r in sm)
+        sm_ms = sum(r["avg_ms"] for r in sm)
+        value, unit = sm_bytes / (sm_ms * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = at[0]["achieved"], "TFLOP/s"
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 softmax math; bf16 MFMA with f32 accumulation (attention)",
+        "data": "synthetic (seeded), resident in HBM",
+        "config": {
+            "workload": ("softmax_large 32768x8192 (fp32 run + bf16 run) + attn_llama13b "
+                         "B8 H40 N2048 D128 causal bf16"),
+            "softmax_rows": 32768, "softmax_cols": 8192,
+            "attn": {"B": 8, "H": 40, "N": 2048, "D": 128, "causal": True},
+            "parallelism": "single GPU",
+        },
+        "value_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4) if unit == "GB/s" else None,
+        "roofline": {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac",
+                                              "traffic")} | {"kernel": dominant["kernel"]},
+        "rooflines": rooflines,
+    }
+    if at:
+        result["attention"] = {"value": at[0]["achieved"], "unit": "TFLOP/s",
+                               "frac_of_bf16_peak": at[0]["frac"],
+                               "flop_convention": "4*D per unmasked (query, key) pair"}
+    if not args.no_cpu_baseline and args.only is None:
+        result["cpu_baseline"] = cpu_baseline(torch, osm_inputs, args.cpu_budget)
+        result["cpu_baseline"]["host_cpus"] = len(os.sched_getaffinity(0))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
