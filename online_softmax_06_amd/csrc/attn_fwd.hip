@@ -3,29 +3,40 @@
 // only in registers.
 //
 // Method ("Ch.6 Softmax and Online Softmax" §6.5-§6.6; xxqk §4.1): a workgroup
-// owns a tile of BM query rows and streams the key/value tiles of its
+// owns a tile of 128 query rows and streams the key/value tiles of its
 // (batch, head) through LDS.  Per tile it forms the scores on the matrix
 // cores, updates the running max m and rescaled sum l of every query row,
-// rescales the output accumulator by alpha = e^(m_old - m_new), and adds
-// P V_j with P = e^(S - m_new) (the form that needs no second correction
-// factor).  The division by l happens once, after the last tile.
+// rescales the output accumulator by alpha = 2^(m_old - m_new), and adds
+// P V_j with P = 2^(S' - m_new) (S' = S * scale * log2 e), the form that needs
+// no second correction factor.  The division by l happens once at the end.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64).  Each wavefront owns
 // 32 query rows and computes the TRANSPOSED products
 //     S^T (keys x queries)  = K   * Q^T      A = K tile (LDS), B = Q (VGPRs)
-//     O^T (dims x queries) += V^T * P^T      A = V^T tile (LDS), B = P (VGPRs)
-// With this orientation every lane holds values of exactly one query row
-// (lane % 32), split with its partner lane (lane ^ 32): row max, row sum and
-// the alpha rescale of the accumulator are per-lane operations plus one
-// permlane32 swap, and P is fed to the second product straight from the
-// registers that received S.  The key order inside each 16-key slice of a
-// tile follows the MFMA output layout; the V^T tile in LDS is stored in that
-// same order, so no register shuffle is needed between the two products.
+//     O^T (dims x queries) += V^T * P^T      A = V^T (LDS),    B = P (VGPRs)
+// so every lane holds values of exactly one query row (lane % 32), shared with
+// its partner lane (lane ^ 32): row max, row sum and the alpha rescale are
+// per-lane operations plus one v_permlane32_swap, and P enters the second
+// product straight from the registers that received S.
 //
-// Data layout in LDS (double-buffered, one barrier per key tile):
-//   K tile   [BN keys][D] bf16, 16-byte units XOR-swizzled by (key & 7).
-//   V^T tile [D][BN keys] bf16, V transposed while it is written, key
-//            positions permuted as above, 16-byte units XOR-swizzled by (d & 7).
+// Memory path.  K and V tiles go from HBM to LDS with buffer_load ... lds
+// (no VGPR staging); keys past the end of the sequence fall outside the
+// buffer descriptor's range and arrive as zeros.  Both tiles are stored
+// row-major ([64 keys][D]) with 16-byte units XOR-swizzled per row.  K rows
+// feed the A operand of the first product with ds_read_b128; V feeds the A
+// operand of the second product through ds_read_b64_tr_b16, which returns
+// each lane four consecutive keys of one head dimension, already transposed.
+// The key order inside every 16-key slice follows the MFMA output layout of
+// S^T, so P needs no register shuffle.  Two LDS stages alternate; one barrier
+// per key tile.
+//
+// Exponent reference.  The reference m used in P = 2^(S' - m) is raised only
+// when a tile's row max exceeds it by more than kLag (in log2 units); P then
+// stays below 2^kLag, which float32 sums and bfloat16 P hold without loss of
+// range, and alpha is exactly 1 on most tiles, so the O rescale is skipped
+// whenever it is 1 for the whole wavefront.  In exact arithmetic the result
+// does not depend on the reference (the combine of §6.4.1 holds for any
+// finite one); the pages' recurrence is the special case kLag = 0.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,100 +48,61 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128;     // query rows per workgroup
 constexpr int kBN = 64;      // keys per tile
 constexpr int kWaves = 4;    // wavefronts per workgroup, 32 query rows each
 constexpr int kThreads = kWaves * 64;
+constexpr float kLag = 8.0f;  // allowed lag of the exponent reference (log2 units)
 
-__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+// Buffer descriptor word 3 for raw (untyped) buffer loads on gfx950.
+constexpr int kBufferFlags = 0x00020000;
+
+#define OSM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Byte offset of 16-byte unit `u` of key row `key` in a K tile.
+// Tile geometry for head dimension D.
 template <int D>
-__device__ __forceinline__ int k_lds_off(int key, int u) {
-  return key * (D * 2) + ((u ^ (key & 7)) << 4);
-}
-
-// Byte offset of the 8-byte chunk holding key positions [4c, 4c+4) of row d
-// in a V^T tile.  Chunks are XOR-swizzled by 2 * (d & 7) so that 16-byte
-// reads stay aligned.
-__device__ __forceinline__ int vt_lds_off(int d, int c) {
-  return d * (kBN * 2) + ((c ^ ((d & 7) << 1)) << 3);
-}
-
-// Position of key `kk` (0..63) inside a V^T row: bits 2 and 3 swapped, which
-// makes the 8 keys one lane feeds to the P V product contiguous.
-__device__ __forceinline__ int vt_pos(int kk) {
-  return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-}
-
-// Per-thread staging registers for one K/V tile.
-template <int D>
-struct TileRegs {
-  static constexpr int kKUnits = kBN * D / 8 / kThreads;  // 16-byte units of K per thread
-  static constexpr int kVThreads = (kBN / 4) * (D / 8);   // threads that carry V (4 keys x 8 dims)
-  uint4 k[kKUnits];
-  uint4 v[4];
+struct Tile {
+  static constexpr int kUnits = D / 8;                // 16-byte units per key row
+  static constexpr int kBytes = kBN * D * 2;          // one K or V tile
+  static constexpr int kLoadsPerWave = kBN * kUnits / 64 / kWaves;  // 1 KB each
+  // Row swizzles of the 16-byte units.  K rows are read 16 bytes per lane
+  // by 32 consecutive rows; V rows are read 8 bytes per lane, 4 consecutive
+  // rows per 16-lane group.
+  __device__ static int k_swz(int row) { return row & (kUnits - 1); }
+  __device__ static int v_swz(int row) { return ((row & 3) << 1) | (D == 128 ? (row & 4) << 1 : 0); }
 };
 
+// Issue the global->LDS copies of one K tile and one V tile (keys
+// [k0, k0 + 64)).  Instruction i of wave w fills LDS units
+// [(w * kLoadsPerWave + i) * 64, +64) of the tile, one 16-byte unit per lane.
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* kg, const uint16_t* vg,
-                                          int k0, int N, int tid) {
-  constexpr int kUnitsPerRow = D / 8;
+__device__ __forceinline__ void issue_tile(char* stage, const uint16_t* kbase,
+                                           const uint16_t* vbase, int head_bytes, int k0, int wave,
+                                           int lane) {
+  // The buffer-to-LDS builtins exist only for the device; the host pass of
+  // this single-source file sees an empty body.
+#if defined(__HIP_DEVICE_COMPILE__)
+  using T = Tile<D>;
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, head_bytes, kBufferFlags);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, head_bytes, kBufferFlags);
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kKUnits; ++i) {
-    const int U = tid + i * kThreads;
-    const int key = U / kUnitsPerRow, u = U % kUnitsPerRow;
-    const int gk = k0 + key;
-    r.k[i] = gk < N ? *reinterpret_cast<const uint4*>(kg + (int64_t)gk * D + u * 8)
-                    : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < T::kLoadsPerWave; ++i) {
+    const int inst = wave * T::kLoadsPerWave + i;
+    const int p = inst * 64 + lane;                 // physical unit in the tile
+    const int row = p / T::kUnits, pu = p % T::kUnits;
+    const int gk = (k0 + row) * (D * 2);            // byte offset of the key row in the head
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, OSM_LDS(stage + inst * 1024), 16,
+                                             gk + ((pu ^ T::k_swz(row)) << 4), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, OSM_LDS(stage + T::kBytes + inst * 1024), 16,
+                                             gk + ((pu ^ T::v_swz(row)) << 4), 0, 0, 0);
   }
-  if (tid < TileRegs<D>::kVThreads) {
-    const int kgrp = tid % (kBN / 4), dg = tid / (kBN / 4);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int gk = k0 + kgrp * 4 + rr;
-      r.v[rr] = gk < N ? *reinterpret_cast<const uint4*>(vg + (int64_t)gk * D + dg * 8)
-                       : make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-// Write the staged tile to LDS: K as is (swizzled), V transposed.
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, char* k_lds, char* vt_lds,
-                                           int tid) {
-  constexpr int kUnitsPerRow = D / 8;
-#pragma unroll
-  for (int i = 0; i < TileRegs<D>::kKUnits; ++i) {
-    const int U = tid + i * kThreads;
-    const int key = U / kUnitsPerRow, u = U % kUnitsPerRow;
-    *reinterpret_cast<uint4*>(k_lds + k_lds_off<D>(key, u)) = r.k[i];
-  }
-  if (tid < TileRegs<D>::kVThreads) {
-    const int kgrp = tid % (kBN / 4), dg = tid / (kBN / 4);
-    const int chunk = vt_pos(kgrp * 4) >> 2;
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.v[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.v[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.v[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.v[3]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      // dims 8*dg + j of keys 4*kgrp .. 4*kgrp+3 -> one 8-byte chunk of row d.
-      const int w = j >> 1;
-      // v_perm_b32 selectors: low halves (bytes 1:0 of each source) for even
-      // j, high halves (bytes 3:2) for odd j.
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      uint2 out;
-      out.x = __builtin_amdgcn_perm(w1[w], w0[w], sel);
-      out.y = __builtin_amdgcn_perm(w3[w], w2[w], sel);
-      const int d = dg * 8 + j;
-      *reinterpret_cast<uint2*>(vt_lds + vt_lds_off(d, chunk)) = out;
-    }
-  }
+#endif
 }
 
 // Map a linear workgroup id to (batch*head, query tile).  Workgroups are
@@ -151,15 +123,111 @@ __device__ __forceinline__ void tile_of(int L, int nqt, int BH, bool causal, int
 }
 
 template <int D, bool kCausal>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
+__device__ __forceinline__ void tile_step(const char* cur, int j, int N, int qw, int qrow, int col,
+                                          int half, int lane, float scale_log2,
+                                          const bf16x8 (&qreg)[D / 16], f32x16 (&oacc)[D / 32],
+                                          float& m_run, float& l_run) {
+  using T = Tile<D>;
+  constexpr int kDC = D / 16;
+  constexpr int kDB = D / 32;
+  const int k0 = j * kBN;
+
+  // A3: S^T for keys [k0, k0 + 64) x this wave's 32 queries.
+  f32x16 s0 = {}, s1 = {};
+#pragma unroll
+  for (int c = 0; c < kDC; ++c) {
+    const int u = 2 * c + half;
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(
+        cur + (col * T::kUnits + (u ^ T::k_swz(col))) * 16);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(
+        cur + ((32 + col) * T::kUnits + (u ^ T::k_swz(32 + col))) * 16);
+    s0 = mfma32(a0, qreg[c], s0);
+    s1 = mfma32(a1, qreg[c], s1);
+  }
+
+  // A4: hide keys past the causal diagonal or past the end of the sequence.
+  const bool need_mask = (kCausal && k0 + kBN - 1 > qw) || (k0 + kBN > N);
+  if (need_mask) {
+    const int lim = kCausal ? min(N, qrow + 1) : N;  // visible keys are < lim
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
+      s0[i] = key < lim ? s0[i] : kNegInf;
+      s1[i] = key + 32 < lim ? s1[i] : kNegInf;
+    }
+  }
+
+  // A5: online-softmax update for this lane's query row.
+  float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+  mx = fmaxf(mx, swap_halves(mx));
+  const float mt = mx * scale_log2;
+  const float m_new = mt > m_run + kLag ? mt : m_run;
+  const float ref = finite_ref(m_new);
+  const float alpha = exp2_hw(m_run - ref);
+  float psum = 0.0f;
+  bf16x8 pb[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    uint32_t w[4];
+#pragma unroll
+    for (int jj = 0; jj < 8; jj += 2) {
+      const float sa = (kc < 2) ? s0[(kc & 1) * 8 + jj] : s1[(kc & 1) * 8 + jj];
+      const float sb = (kc < 2) ? s0[(kc & 1) * 8 + jj + 1] : s1[(kc & 1) * 8 + jj + 1];
+      const float pa = exp2_hw(__builtin_fmaf(sa, scale_log2, -ref));
+      const float pbv = exp2_hw(__builtin_fmaf(sb, scale_log2, -ref));
+      psum += pa + pbv;
+      w[jj / 2] = pack_bf16x2(pa, pbv);
+    }
+    pb[kc] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+
+  // A6: rescale the accumulator (skipped when alpha is 1 on every lane),
+  // then O^T += V^T P^T.
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int b = 0; b < kDB; ++b) oacc[b] *= alpha;
+  }
+  // Transposed V reads: lane (group g = lane / 16, r = lane % 16) supplies the
+  // address of dims [d0 + 4 (r % 4), +4) of key row base + r / 4; it receives
+  // dims d0 + r of keys base .. base + 3 (d0 = 32 b + 16 (g % 2)).
+  const int g = lane >> 4, r = lane & 15;
+  const int vkey = half * 4 + (r >> 2);               // 0..7 within a 16-key slice
+  const int vd = (g & 1) * 16 + 4 * (r & 3);          // dim offset within a 32-dim block
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+    for (int b = 0; b < kDB; ++b) {
+      const int d = b * 32 + vd;
+      const int row0 = kc * 16 + vkey, row1 = row0 + 8;
+      const char* p0 = cur + T::kBytes + row0 * (D * 2) +
+                       (((d >> 3) ^ T::v_swz(row0)) << 4) + (d & 7) * 2;
+      const char* p1 = cur + T::kBytes + row1 * (D * 2) +
+                       (((d >> 3) ^ T::v_swz(row1)) << 4) + (d & 7) * 2;
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(p0));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(p1));
+      const bf16x8 a = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[b] = mfma32(a, pb[kc], oacc[b]);
+    }
+  }
+}
+
+template <int D, bool kCausal>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int BH,
     int N, float scale_log2) {
-  constexpr int kDC = D / 16;  // 16-wide slices of the head dimension
-  constexpr int kDB = D / 32;  // 32-row blocks of O^T
-  constexpr int kKBytes = kBN * D * 2;
-  constexpr int kVBytes = D * kBN * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * (kKBytes + kVBytes)];
+  using T = Tile<D>;
+  constexpr int kDC = D / 16;
+  constexpr int kDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char stage0[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char stage1[2 * T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,115 +239,51 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   int bh, qt;
   tile_of(blockIdx.x, nqt, BH, kCausal, bh, qt);
   const int64_t head_off = (int64_t)bh * N * D;
-  const uint16_t* qg = q + head_off;
-  const uint16_t* kg = k + head_off;
-  const uint16_t* vg = v + head_off;
+  const int head_bytes = N * D * 2;
+  const uint16_t* kh = k + head_off;
+  const uint16_t* vh = v + head_off;
 
   const int q0 = qt * kBM;
   const int qw = q0 + wave * 32;  // first query row of this wave
   const int qrow = qw + col;      // this lane's query row
   const bool wave_live = qw < N;
 
+  const int kv_end = kCausal ? min(N, q0 + kBM) : N;
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+  issue_tile<D>(stage0, kh, vh, head_bytes, 0, wave, lane);
+
   // A1: this lane's part of Q as the B operand of S^T = K Q^T.
-  uint4 qreg[kDC];
+  bf16x8 qreg[kDC];
+  const uint16_t* qg = q + head_off + (int64_t)qrow * D + half * 8;
 #pragma unroll
   for (int c = 0; c < kDC; ++c) {
-    qreg[c] = qrow < N ? *reinterpret_cast<const uint4*>(qg + (int64_t)qrow * D + c * 16 + half * 8)
-                       : make_uint4(0, 0, 0, 0);
+    qreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(qg + c * 16) : bf16x8{};
   }
 
   f32x16 oacc[kDB];
 #pragma unroll
   for (int b = 0; b < kDB; ++b) oacc[b] = f32x16{};
-  float m_run = kNegInf;  // running max, in units of log2(e) * scale * S
+  float m_run = kNegInf;  // exponent reference, in units of log2(e) * scale * S
   float l_run = 0.0f;     // this lane's half of the running sum
 
-  const int kv_end = kCausal ? min(N, q0 + kBM) : N;
-  const int ntiles = (kv_end + kBN - 1) / kBN;
-
-  TileRegs<D> stage;
-  load_tile<D>(stage, kg, vg, 0, N, tid);
-  store_tile<D>(stage, smem, smem + kKBytes, tid);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int k0 = j * kBN;
-    char* k_lds = smem + (j & 1) * (kKBytes + kVBytes);
-    char* vt_lds = k_lds + kKBytes;
-    const bool has_next = j + 1 < ntiles;
-    // A2: prefetch the next tile into registers while this one is used.
-    if (has_next) load_tile<D>(stage, kg, vg, k0 + kBN, N, tid);
-
-    const bool visible = wave_live && (!kCausal || k0 <= qw + 31);
-    if (visible) {
-      // A3: S^T for keys [k0, k0+64) x this wave's 32 queries.
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int c = 0; c < kDC; ++c) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint4 a =
-              *reinterpret_cast<const uint4*>(k_lds + k_lds_off<D>(kb * 32 + col, 2 * c + half));
-          sacc[kb] = mfma32(a, qreg[c], sacc[kb]);
-        }
-      }
-      // A4: mask keys past the causal diagonal or past the end of the sequence.
-      const bool need_mask = (kCausal && k0 + kBN - 1 > qw) || (k0 + kBN > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            const bool hide = key >= N || (kCausal && key > qrow);
-            if (hide) sacc[kb][i] = kNegInf;
-          }
-        }
-      }
-      // A5: online-softmax update of (m, l) for this lane's query row.
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float ref = finite_ref(m_new);
-      const float alpha = exp2_hw(m_run - ref);
-      float psum = 0.0f;
-      uint4 pb[4];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        float p[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          p[jj] = exp2_hw(__builtin_fmaf(sacc[kc >> 1][(kc & 1) * 8 + jj], scale_log2, -ref));
-          psum += p[jj];
-        }
-        pb[kc] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      // A6: rescale the accumulator, then O^T += V^T P^T.
-#pragma unroll
-      for (int b = 0; b < kDB; ++b) oacc[b] *= alpha;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-        for (int b = 0; b < kDB; ++b) {
-          const uint4 a = *reinterpret_cast<const uint4*>(
-              vt_lds + vt_lds_off(b * 32 + col, (kc * 16 + half * 8) >> 2));
-          oacc[b] = mfma32(a, pb[kc], oacc[b]);
-        }
-      }
-    }
-
-    if (has_next) {
-      store_tile<D>(stage, smem + ((j + 1) & 1) * (kKBytes + kVBytes),
-                    smem + ((j + 1) & 1) * (kKBytes + kVBytes) + kKBytes, tid);
-    }
+  // A2: tile j is computed from one stage while tile j + 1 streams into the
+  // other.  The wait + barrier at the top of each step makes tile j visible
+  // and guarantees every wave has finished reading the stage about to be
+  // refilled.
+  for (int j = 0; j < ntiles; j += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (j + 1 < ntiles) issue_tile<D>(stage1, kh, vh, head_bytes, (j + 1) * kBN, wave, lane);
+    if (wave_live && (!kCausal || j * kBN <= qw + 31))
+      tile_step<D, kCausal>(stage0, j, N, qw, qrow, col, half, lane, scale_log2, qreg, oacc,
+                            m_run, l_run);
+    if (j + 1 >= ntiles) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 2 < ntiles) issue_tile<D>(stage0, kh, vh, head_bytes, (j + 2) * kBN, wave, lane);
+    if (wave_live && (!kCausal || (j + 1) * kBN <= qw + 31))
+      tile_step<D, kCausal>(stage1, j + 1, N, qw, qrow, col, half, lane, scale_log2, qreg, oacc,
+                            m_run, l_run);
   }
 
   // A7: O = O / l (deferred division), LSE = ln 2 * (m + log2 l).
@@ -290,12 +294,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 #pragma unroll
     for (int b = 0; b < kDB; ++b) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // O^T rows b*32 + g*8 + half*4 + (0..3): four consecutive dims.
+      for (int gq = 0; gq < 4; ++gq) {
+        // O^T rows b*32 + gq*8 + half*4 + (0..3): four consecutive dims.
         uint2 w;
-        w.x = pack_bf16x2(oacc[b][g * 4 + 0] * inv, oacc[b][g * 4 + 1] * inv);
-        w.y = pack_bf16x2(oacc[b][g * 4 + 2] * inv, oacc[b][g * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + b * 32 + g * 8 + half * 4) = w;
+        w.x = pack_bf16x2(oacc[b][gq * 4 + 0] * inv, oacc[b][gq * 4 + 1] * inv);
+        w.y = pack_bf16x2(oacc[b][gq * 4 + 2] * inv, oacc[b][gq * 4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + b * 32 + gq * 8 + half * 4) = w;
       }
     }
     if (half == 0) {

@@ -61,6 +61,8 @@ int osm_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     return OSM_ERR_INVALID_ARG;
   // One 256-thread workgroup per 128 query rows of each (batch, head): the
   // launch must stay below 2^32 work-items.
+  // Key/value tiles are addressed with 32-bit buffer offsets within one head.
+  if (((int64_t)N + 64) * D * 2 >= ((int64_t)1 << 31)) return OSM_ERR_UNSUPPORTED;
   const int64_t workgroups = bh * (((int64_t)N + 127) / 128);
   if (workgroups * 256 >= ((int64_t)1 << 32)) return OSM_ERR_UNSUPPORTED;
   return from_hip(osm::attn_fwd_launch(q, k, v, o, lse, B, H, N, D, scale, causal != 0,
