@@ -23,10 +23,14 @@ SOURCES = ["osm_api.cpp", "softmax_rows.hip", "attn_fwd.hip"]
 
 ARCH = "gfx950"
 
-# Packed-FP32 instructions are kept out of the generated code; no fast-math
-# flag is used, because the -inf guards of the online softmax must survive.
+# Packed-FP32 instructions are kept out of the generated code.  No fast-math
+# flag is used: infinities are honoured, because the -inf guards of the online
+# softmax must survive.  NaN inputs are outside the contract, so NaNs are not
+# honoured; that lets max reductions compile to v_max3_f32 without an extra
+# quieting instruction per operand.
 HIPCC_FLAGS = [
     "-O3",
+    "-fno-honor-nans",
     "-std=c++17",
     f"--offload-arch={ARCH}",
     "-fPIC",

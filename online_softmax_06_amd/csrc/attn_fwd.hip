@@ -71,36 +71,40 @@ struct Tile {
   static constexpr int kUnits = D / 8;                // 16-byte units per key row
   static constexpr int kBytes = kBN * D * 2;          // one K or V tile
   static constexpr int kLoadsPerWave = kBN * kUnits / 64 / kWaves;  // 1 KB each
-  // Row swizzles of the 16-byte units.  K rows are read 16 bytes per lane
-  // by 32 consecutive rows; V rows are read 8 bytes per lane, 4 consecutive
-  // rows per 16-lane group.
+  // Row swizzles of the 16-byte units (LDS has 64 four-byte banks).
+  // K rows are read 16 bytes per lane, 16 consecutive rows per 256-byte bank
+  // sweep: XOR by row & 15 (row & 7 at D = 64) spreads them over all banks.
+  // V rows are read 8 bytes per lane through the transpose read: each 32-lane
+  // half reads 4 consecutive rows x 64 bytes, so rows r..r+3 are XORed by
+  // 0, 4, 8, 12 units (one 64-byte quarter each) and rows 4..7 of an 8-row
+  // group additionally by 2.  Every swizzle depends on row & 7 or row & 15
+  // only, so rows 32 apart (K) and 8 or 16 apart (V) share one lane offset.
   __device__ static int k_swz(int row) { return row & (kUnits - 1); }
-  __device__ static int v_swz(int row) { return ((row & 3) << 1) | (D == 128 ? (row & 4) << 1 : 0); }
+  __device__ static int v_swz(int row) {
+    return D == 128 ? (((row & 3) << 2) | ((row & 4) >> 1)) : ((row & 3) << 1);
+  }
 };
 
-// Issue the global->LDS copies of one K tile and one V tile (keys
-// [k0, k0 + 64)).  Instruction i of wave w fills LDS units
-// [(w * kLoadsPerWave + i) * 64, +64) of the tile, one 16-byte unit per lane.
-template <int D>
-__device__ __forceinline__ void issue_tile(char* stage, const uint16_t* kbase,
-                                           const uint16_t* vbase, int head_bytes, int k0, int wave,
-                                           int lane) {
+// Issue the global->LDS copy of one K or V tile (keys [k0, k0 + 64)) into
+// `buf`.  Instruction i of wave w fills LDS units [(w * kLoadsPerWave + i) *
+// 64, +64) of the tile, one 16-byte unit per lane; `swz` is the tile's row
+// swizzle.  Keys at or past the end of the head read as zeros.
+template <int D, int (*Swz)(int)>
+__device__ __forceinline__ void issue_tile(char* buf, const uint16_t* base, int head_bytes, int k0,
+                                           int wave, int lane) {
   // The buffer-to-LDS builtins exist only for the device; the host pass of
   // this single-source file sees an empty body.
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = Tile<D>;
-  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, head_bytes, kBufferFlags);
-  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, head_bytes, kBufferFlags);
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, head_bytes, kBufferFlags);
 #pragma unroll
   for (int i = 0; i < T::kLoadsPerWave; ++i) {
     const int inst = wave * T::kLoadsPerWave + i;
     const int p = inst * 64 + lane;                 // physical unit in the tile
     const int row = p / T::kUnits, pu = p % T::kUnits;
-    const int gk = (k0 + row) * (D * 2);            // byte offset of the key row in the head
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, OSM_LDS(stage + inst * 1024), 16,
-                                             gk + ((pu ^ T::k_swz(row)) << 4), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, OSM_LDS(stage + T::kBytes + inst * 1024), 16,
-                                             gk + ((pu ^ T::v_swz(row)) << 4), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, OSM_LDS(buf + inst * 1024), 16,
+                                             (k0 + row) * (D * 2) + ((pu ^ Swz(row)) << 4), 0, 0,
+                                             0);
   }
 #endif
 }
@@ -122,46 +126,102 @@ __device__ __forceinline__ void tile_of(int L, int nqt, int BH, bool causal, int
   qt = causal ? nqt - 1 - rank : rank;
 }
 
-template <int D, bool kCausal>
-__device__ __forceinline__ void tile_step(const char* cur, int j, int N, int qw, int qrow, int col,
-                                          int half, int lane, float scale_log2,
-                                          const bf16x8 (&qreg)[D / 16], f32x16 (&oacc)[D / 32],
-                                          float& m_run, float& l_run) {
-  using T = Tile<D>;
-  constexpr int kDC = D / 16;
-  constexpr int kDB = D / 32;
-  const int k0 = j * kBN;
+// Per-lane LDS byte offsets inside a K or V buffer, computed once per
+// workgroup.
+// K: lane reads row `col` (and col + 32), 16-byte unit (2c + half) ^ swz(col);
+// since the swizzle keeps bit 0 of the unit apart from c's bits, the offset
+// for slice c is k ^ (c << 5), and rows col + 32 sit 32 rows further.
+// V: lane reads key row `vkey` (+ 16 kc + 8 part) at dims b*32 + vd; the
+// swizzle depends on row & 7 only, so the other rows are constant offsets.
+template <int D>
+struct LaneOffsets {
+  int k;
+  int v[D / 32];
+};
 
-  // A3: S^T for keys [k0, k0 + 64) x this wave's 32 queries.
-  f32x16 s0 = {}, s1 = {};
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
+  using T = Tile<D>;
+  const int col = lane & 31, half = lane >> 5;
+  LaneOffsets<D> off;
+  off.k = col * (D * 2) + ((half ^ T::k_swz(col)) << 4);
+  const int g = lane >> 4, r = lane & 15;
+  const int vkey = half * 4 + (r >> 2);        // 0..7 within a 16-key slice
+  const int vd = (g & 1) * 16 + 4 * (r & 3);   // dim offset within a 32-dim block
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) {
+    const int d = b * 32 + vd;
+    off.v[b] = vkey * (D * 2) + (((d >> 3) ^ T::v_swz(vkey)) << 4) + (d & 7) * 2;
+  }
+  return off;
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+}
+
+// A3: S^T = K Q^T for one key tile (16 products at D = 128) from `kbuf`.
+// K operands are read two slices ahead of the products that use them.
+template <int D>
+__device__ __forceinline__ void compute_scores(const char* kbuf, const LaneOffsets<D>& off,
+                                               const bf16x8 (&qreg)[D / 16], f32x16 (&s)[2]) {
+  constexpr int kDC = D / 16;
+  constexpr int kRow = D * 2;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+  bf16x8 ka[3][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const char* pk = kbuf + (off.k ^ (c << 5));
+    ka[c][0] = *reinterpret_cast<const bf16x8*>(pk);
+    ka[c][1] = *reinterpret_cast<const bf16x8*>(pk + 32 * kRow);
+  }
 #pragma unroll
   for (int c = 0; c < kDC; ++c) {
-    const int u = 2 * c + half;
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(
-        cur + (col * T::kUnits + (u ^ T::k_swz(col))) * 16);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(
-        cur + ((32 + col) * T::kUnits + (u ^ T::k_swz(32 + col))) * 16);
-    s0 = mfma32(a0, qreg[c], s0);
-    s1 = mfma32(a1, qreg[c], s1);
+    if (c + 2 < kDC) {
+      const char* pk = kbuf + (off.k ^ ((c + 2) << 5));
+      ka[(c + 2) % 3][0] = *reinterpret_cast<const bf16x8*>(pk);
+      ka[(c + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(pk + 32 * kRow);
+    }
+    s[0] = mfma32(ka[c % 3][0], qreg[c], s[0]);
+    s[1] = mfma32(ka[c % 3][1], qreg[c], s[1]);
   }
+}
+
+// One key tile j for one wavefront: mask and softmax the scores S_j held in
+// `scur`, then O^T += V_j^T P_j^T; with kNext, then form the scores of tile
+// j + 1 into `snext`, so 32 matrix products run back to back per tile.
+template <int D, bool kCausal, bool kNext>
+__device__ __forceinline__ void tile_step(const char* kbuf_next, const char* vbuf,
+                                          const LaneOffsets<D>& off, int j, int N, int qw,
+                                          int qrow, int half, float scale_log2,
+                                          const bf16x8 (&qreg)[D / 16], f32x16 (&scur)[2],
+                                          f32x16 (&snext)[2], f32x16 (&oacc)[D / 32],
+                                          float& m_run, float& l_run) {
+  constexpr int kDC = D / 16;
+  constexpr int kDB = D / 32;
+  constexpr int kRow = D * 2;  // bytes per key row
+  const int k0 = j * kBN;
 
   // A4: hide keys past the causal diagonal or past the end of the sequence.
   const bool need_mask = (kCausal && k0 + kBN - 1 > qw) || (k0 + kBN > N);
   if (need_mask) {
-    const int lim = kCausal ? min(N, qrow + 1) : N;  // visible keys are < lim
+    // Keys k0 + (i / 4) * 8 + half * 4 + i % 4 (+ 32) are visible when below
+    // lim; compare the constant part against lim - k0 - 4 * half.
+    const int lim = (kCausal ? min(N, qrow + 1) : N) - k0 - half * 4;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
-      s0[i] = key < lim ? s0[i] : kNegInf;
-      s1[i] = key + 32 < lim ? s1[i] : kNegInf;
+      const int kk = (i >> 2) * 8 + (i & 3);
+      scur[0][i] = kk < lim ? scur[0][i] : kNegInf;
+      scur[1][i] = kk + 32 < lim ? scur[1][i] : kNegInf;
     }
   }
 
   // A5: online-softmax update for this lane's query row.
-  float mx = fmaxf(s0[0], s1[0]);
+  float mx = __builtin_fmaxf(scur[0][0], scur[1][0]);
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-  mx = fmaxf(mx, swap_halves(mx));
+  for (int i = 1; i < 16; ++i) mx = max3(mx, scur[0][i], scur[1][i]);
+  mx = __builtin_fmaxf(mx, swap_halves(mx));
   const float mt = mx * scale_log2;
   const float m_new = mt > m_run + kLag ? mt : m_run;
   const float ref = finite_ref(m_new);
@@ -173,8 +233,8 @@ __device__ __forceinline__ void tile_step(const char* cur, int j, int N, int qw,
     uint32_t w[4];
 #pragma unroll
     for (int jj = 0; jj < 8; jj += 2) {
-      const float sa = (kc < 2) ? s0[(kc & 1) * 8 + jj] : s1[(kc & 1) * 8 + jj];
-      const float sb = (kc < 2) ? s0[(kc & 1) * 8 + jj + 1] : s1[(kc & 1) * 8 + jj + 1];
+      const float sa = scur[kc >> 1][(kc & 1) * 8 + jj];
+      const float sb = scur[kc >> 1][(kc & 1) * 8 + jj + 1];
       const float pa = exp2_hw(__builtin_fmaf(sa, scale_log2, -ref));
       const float pbv = exp2_hw(__builtin_fmaf(sb, scale_log2, -ref));
       psum += pa + pbv;
@@ -188,34 +248,31 @@ __device__ __forceinline__ void tile_step(const char* cur, int j, int N, int qw,
   // A6: rescale the accumulator (skipped when alpha is 1 on every lane),
   // then O^T += V^T P^T.
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    // The empty asm keeps this a branch: without it the compiler would
+    // multiply unconditionally, since scaling by 1 is harmless.
+    asm volatile("");
 #pragma unroll
     for (int b = 0; b < kDB; ++b) oacc[b] *= alpha;
   }
   // Transposed V reads: lane (group g = lane / 16, r = lane % 16) supplies the
   // address of dims [d0 + 4 (r % 4), +4) of key row base + r / 4; it receives
   // dims d0 + r of keys base .. base + 3 (d0 = 32 b + 16 (g % 2)).
-  const int g = lane >> 4, r = lane & 15;
-  const int vkey = half * 4 + (r >> 2);               // 0..7 within a 16-key slice
-  const int vd = (g & 1) * 16 + 4 * (r & 3);          // dim offset within a 32-dim block
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
     for (int b = 0; b < kDB; ++b) {
-      const int d = b * 32 + vd;
-      const int row0 = kc * 16 + vkey, row1 = row0 + 8;
-      const char* p0 = cur + T::kBytes + row0 * (D * 2) +
-                       (((d >> 3) ^ T::v_swz(row0)) << 4) + (d & 7) * 2;
-      const char* p1 = cur + T::kBytes + row1 * (D * 2) +
-                       (((d >> 3) ^ T::v_swz(row1)) << 4) + (d & 7) * 2;
+      const char* p0 = vbuf + off.v[b] + kc * 16 * kRow;
       const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4*)(p0));
       const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(p1));
+          (__attribute__((address_space(3))) s16x4*)(p0 + 8 * kRow));
       const bf16x8 a = __builtin_bit_cast(
           bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[b] = mfma32(a, pb[kc], oacc[b]);
     }
   }
+  // A3 for tile j + 1: its products follow this tile's in one stream.
+  if constexpr (kNext) compute_scores<D>(kbuf_next, off, qreg, snext);
 }
 
 template <int D, bool kCausal>
@@ -226,8 +283,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   using T = Tile<D>;
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char stage0[2 * T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char stage1[2 * T::kBytes];
+  // Two K buffers and two V buffers: tile j's K sits in kbuf[j & 1], its V in
+  // vbuf[j & 1].
+  __shared__ __attribute__((aligned(1024))) char kbuf0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -246,11 +307,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int q0 = qt * kBM;
   const int qw = q0 + wave * 32;  // first query row of this wave
   const int qrow = qw + col;      // this lane's query row
-  const bool wave_live = qw < N;
 
   const int kv_end = kCausal ? min(N, q0 + kBM) : N;
   const int ntiles = (kv_end + kBN - 1) / kBN;
-  issue_tile<D>(stage0, kh, vh, head_bytes, 0, wave, lane);
+  // Last key tile with work for this wave (-1: the wave is past the end).
+  const int jw_last = qw >= N ? -1 : (kCausal ? min(ntiles - 1, (qw + 31) / kBN) : ntiles - 1);
+
+  // A2 prologue: K_0, V_0 and K_1 in flight.
+  issue_tile<D, T::k_swz>(kbuf0, kh, head_bytes, 0, wave, lane);
+  issue_tile<D, T::v_swz>(vbuf0, vh, head_bytes, 0, wave, lane);
+  if (ntiles > 1) issue_tile<D, T::k_swz>(kbuf1, kh, head_bytes, kBN, wave, lane);
 
   // A1: this lane's part of Q as the B operand of S^T = K Q^T.
   bf16x8 qreg[kDC];
@@ -260,30 +326,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     qreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(qg + c * 16) : bf16x8{};
   }
 
+  const LaneOffsets<D> off = lane_offsets<D>(lane);
   f32x16 oacc[kDB];
 #pragma unroll
   for (int b = 0; b < kDB; ++b) oacc[b] = f32x16{};
   float m_run = kNegInf;  // exponent reference, in units of log2(e) * scale * S
   float l_run = 0.0f;     // this lane's half of the running sum
+  f32x16 sA[2], sB[2];    // scores of the current and the next tile
 
-  // A2: tile j is computed from one stage while tile j + 1 streams into the
-  // other.  The wait + barrier at the top of each step makes tile j visible
-  // and guarantees every wave has finished reading the stage about to be
-  // refilled.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (jw_last >= 0) compute_scores<D>(kbuf0, off, qreg, sA);
+
+  // A2: at the top of step j, K_{j+1} and V_j have landed and every wave is
+  // done with the buffers of K_j and V_{j-1}, which then receive K_{j+2} and
+  // V_{j+1}.  One barrier per key tile.
   for (int j = 0; j < ntiles; j += 2) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < ntiles) issue_tile<D>(stage1, kh, vh, head_bytes, (j + 1) * kBN, wave, lane);
-    if (wave_live && (!kCausal || j * kBN <= qw + 31))
-      tile_step<D, kCausal>(stage0, j, N, qw, qrow, col, half, lane, scale_log2, qreg, oacc,
-                            m_run, l_run);
+    if (j + 2 < ntiles) issue_tile<D, T::k_swz>(kbuf0, kh, head_bytes, (j + 2) * kBN, wave, lane);
+    if (j + 1 < ntiles) issue_tile<D, T::v_swz>(vbuf1, vh, head_bytes, (j + 1) * kBN, wave, lane);
+    if (j < jw_last) {
+      tile_step<D, kCausal, true>(kbuf1, vbuf0, off, j, N, qw, qrow, half, scale_log2, qreg, sA,
+                                  sB, oacc, m_run, l_run);
+    } else if (j == jw_last) {
+      tile_step<D, kCausal, false>(kbuf1, vbuf0, off, j, N, qw, qrow, half, scale_log2, qreg, sA,
+                                   sB, oacc, m_run, l_run);
+    }
     if (j + 1 >= ntiles) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 2 < ntiles) issue_tile<D>(stage0, kh, vh, head_bytes, (j + 2) * kBN, wave, lane);
-    if (wave_live && (!kCausal || (j + 1) * kBN <= qw + 31))
-      tile_step<D, kCausal>(stage1, j + 1, N, qw, qrow, col, half, lane, scale_log2, qreg, oacc,
-                            m_run, l_run);
+    if (j + 3 < ntiles) issue_tile<D, T::k_swz>(kbuf1, kh, head_bytes, (j + 3) * kBN, wave, lane);
+    if (j + 2 < ntiles) issue_tile<D, T::v_swz>(vbuf0, vh, head_bytes, (j + 2) * kBN, wave, lane);
+    if (j + 1 < jw_last) {
+      tile_step<D, kCausal, true>(kbuf0, vbuf1, off, j + 1, N, qw, qrow, half, scale_log2, qreg,
+                                  sB, sA, oacc, m_run, l_run);
+    } else if (j + 1 == jw_last) {
+      tile_step<D, kCausal, false>(kbuf0, vbuf1, off, j + 1, N, qw, qrow, half, scale_log2, qreg,
+                                   sB, sA, oacc, m_run, l_run);
+    }
   }
 
   // A7: O = O / l (deferred division), LSE = ln 2 * (m + log2 l).
