@@ -74,6 +74,30 @@ int osm_softmax_rows(const void* in, void* out, int64_t rows, int64_t cols, int 
                      void* stream);
 
 /*
+ * osm_softmax_rows_ex -- row softmax with a fused additive mask and/or
+ * per-row lengths.
+ *
+ * The fused form of [Ch6 §6.7.3]: each logit is in[r, i] + mask[r % mask_rows,
+ * i] (a mask of 0 / -inf hides entries, other finite values bias them), and
+ * with row_len only the first row_len[r] entries of row r take part; the
+ * outputs past a row's length are 0.  Everything else is as in
+ * osm_softmax_rows (one read of in and mask, one write of out).
+ *
+ *   mask       device pointer, same dtype as in, contiguous [mask_rows, cols];
+ *              NULL for no mask.  mask_rows >= 1 when mask is given (1
+ *              broadcasts one mask row to every row).  The sum is formed in
+ *              float32.
+ *   row_len    device pointer to int32 [rows], or NULL for full rows; values
+ *              are clamped to [0, cols] (0 gives an all-zero row).
+ *
+ * Returns as osm_softmax_rows, plus OSM_ERR_INVALID_ARG for mask_rows < 1
+ * with a mask, or a misaligned mask / row_len pointer.
+ */
+int osm_softmax_rows_ex(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                        const void* mask, int64_t mask_rows, const int32_t* row_len,
+                        void* stream);
+
+/*
  * osm_attn_fwd -- fused attention forward with per-row log-sum-exp.
  *
  * For every batch b, head h and query row i:
@@ -99,10 +123,39 @@ int osm_softmax_rows(const void* in, void* out, int64_t rows, int64_t cols, int 
  *
  * Returns OSM_OK, OSM_ERR_INVALID_ARG (null pointer with nonzero size, negative
  * size, B*H*N*D overflowing int64, non-finite or non-positive scale, pointer
- * not 16-byte aligned), OSM_ERR_UNSUPPORTED (D not 64 or 128), or OSM_ERR_HIP.
+ * not 16-byte aligned), OSM_ERR_UNSUPPORTED (D not 64 or 128; (N + 64) * D * 2
+ * >= 2^31 bytes per head; more than 2^24 workgroups), or OSM_ERR_HIP.
  */
 int osm_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int H, int N, int D, float scale, int causal, void* stream);
+
+/*
+ * osm_attn_fwd_ex -- fused attention forward with key padding and an
+ * additive score bias.
+ *
+ *   S[i, j] = scale * dot(q[b,h,i,:], k[b,h,j,:]) + bias[b,h,i,j]
+ *   hidden (-inf) when j >= kv_len[b], or when causal and j > i
+ * ([xxqk §6.3]: additive -inf masks; [Ch6 §6.7.3]: the mask fused into the
+ * softmax).  o and lse are then as in osm_attn_fwd; a query row with no
+ * visible key gets o = 0 and lse = -inf.
+ *
+ *   kv_len          device pointer to int32 [B] (valid keys per batch,
+ *                   clamped to [0, N]), or NULL for N.  Key tiles past a
+ *                   batch's length are not visited.
+ *   bias            device pointer to float32, element (b, h, i, j) at
+ *                   bias[b * bias_stride_b + h * bias_stride_h + i * N + j]
+ *                   (strides in elements, >= 0; 0 broadcasts), or NULL.
+ *                   4-byte alignment required; 16-byte alignment with N and
+ *                   both strides multiples of 4 takes 16-byte loads.
+ *   bias_stride_b, bias_stride_h   ignored when bias is NULL.
+ *
+ * Returns as osm_attn_fwd, plus OSM_ERR_INVALID_ARG for negative strides or a
+ * misaligned kv_len / bias pointer.
+ */
+int osm_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int N, int D, float scale, int causal, const int32_t* kv_len,
+                    const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                    void* stream);
 
 /* Human-readable name of a status code; never NULL, static storage. */
 const char* osm_status_string(int status);

@@ -8,13 +8,18 @@ Raw entry points, same names and arguments as the C ABI (device pointers as
 ints; ``stream`` is a hipStream_t handle, 0 for the null stream):
 
     osm_softmax_rows(in_ptr, out_ptr, rows, cols, dtype, stream) -> status
+    osm_softmax_rows_ex(in_ptr, out_ptr, rows, cols, dtype, mask, mask_rows,
+                        row_len, stream) -> status
     osm_attn_fwd(q, k, v, o, lse, B, H, N, D, scale, causal, stream) -> status
+    osm_attn_fwd_ex(q, k, v, o, lse, B, H, N, D, scale, causal, kv_len, bias,
+                    bias_stride_b, bias_stride_h, stream) -> status
     osm_status_string(status) -> str
 
 Tensor-level helpers:
 
-    softmax_rows(x, out=None) -> Tensor
-    attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None) -> (o, lse)
+    softmax_rows(x, out=None, mask=None, row_len=None) -> Tensor
+    attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None,
+             kv_len=None, bias=None) -> (o, lse)
 
 If the library has not been built, every call raises ``RuntimeError``; there
 is no fallback implementation.
@@ -26,8 +31,9 @@ import os
 
 __all__ = [
     "OSM_F32", "OSM_BF16", "OSM_OK", "OSM_ERR_INVALID_ARG", "OSM_ERR_UNSUPPORTED", "OSM_ERR_HIP",
-    "OsmError", "lib_path", "load_library", "osm_softmax_rows", "osm_attn_fwd",
-    "osm_status_string", "osm_version", "softmax_rows", "attn_fwd",
+    "OsmError", "lib_path", "load_library", "osm_softmax_rows", "osm_softmax_rows_ex",
+    "osm_attn_fwd", "osm_attn_fwd_ex", "osm_status_string", "osm_version", "softmax_rows",
+    "attn_fwd",
 ]
 
 OSM_F32, OSM_BF16 = 0, 1
@@ -63,6 +69,11 @@ def load_library():
     c_vp, c_i64, c_int, c_f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     lib.osm_softmax_rows.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_vp]
     lib.osm_softmax_rows.restype = c_int
+    lib.osm_softmax_rows_ex.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_i64, c_vp, c_vp]
+    lib.osm_softmax_rows_ex.restype = c_int
+    lib.osm_attn_fwd_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                    c_f, c_int, c_vp, c_vp, c_i64, c_i64, c_vp]
+    lib.osm_attn_fwd_ex.restype = c_int
     lib.osm_attn_fwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_f,
                                  c_int, c_vp]
     lib.osm_attn_fwd.restype = c_int
@@ -82,8 +93,21 @@ def osm_softmax_rows(in_ptr, out_ptr, rows, cols, dtype, stream=0):
     return load_library().osm_softmax_rows(in_ptr, out_ptr, rows, cols, dtype, stream)
 
 
+def osm_softmax_rows_ex(in_ptr, out_ptr, rows, cols, dtype, mask=0, mask_rows=0, row_len=0,
+                        stream=0):
+    return load_library().osm_softmax_rows_ex(in_ptr, out_ptr, rows, cols, dtype, mask or None,
+                                              mask_rows, row_len or None, stream)
+
+
 def osm_attn_fwd(q, k, v, o, lse, B, H, N, D, scale, causal, stream=0):
     return load_library().osm_attn_fwd(q, k, v, o, lse, B, H, N, D, scale, int(causal), stream)
+
+
+def osm_attn_fwd_ex(q, k, v, o, lse, B, H, N, D, scale, causal, kv_len=0, bias=0,
+                    bias_stride_b=0, bias_stride_h=0, stream=0):
+    return load_library().osm_attn_fwd_ex(q, k, v, o, lse, B, H, N, D, scale, int(causal),
+                                          kv_len or None, bias or None, bias_stride_b,
+                                          bias_stride_h, stream)
 
 
 def osm_status_string(status):
@@ -117,11 +141,14 @@ def _dtype_code(dtype):
     raise TypeError(f"softmax_rows supports float32 and bfloat16, not {dtype}")
 
 
-def softmax_rows(x, out=None):
+def softmax_rows(x, out=None, mask=None, row_len=None):
     """Softmax over the last dimension of a contiguous CUDA tensor.
 
     ``x`` is viewed as [rows, cols] with cols = x.shape[-1].  ``out`` may be
     ``x`` itself (in place) or a new tensor of the same shape and dtype.
+    ``mask`` (same dtype, contiguous, viewed as [mask_rows, cols]; row r uses
+    mask row r % mask_rows) is added to the logits; ``row_len`` (int32 CUDA
+    tensor of length rows) limits each row, the rest of the row becoming 0.
     """
     torch = _torch()
     if not x.is_cuda:
@@ -136,17 +163,32 @@ def softmax_rows(x, out=None):
         raise ValueError("out must be a contiguous tensor of the same shape, dtype and device")
     cols = x.shape[-1] if x.dim() > 0 else 1
     rows = x.numel() // cols if cols else 0
-    st = osm_softmax_rows(x.data_ptr(), out.data_ptr(), rows, cols, code, _stream_handle(x.device))
+    mask_ptr, mask_rows, len_ptr = 0, 0, 0
+    if mask is not None:
+        if not mask.is_cuda or mask.dtype != x.dtype or not mask.is_contiguous() \
+                or mask.shape[-1] != cols or mask.numel() == 0:
+            raise ValueError("mask must be a contiguous CUDA tensor of x's dtype ending in cols")
+        mask_ptr, mask_rows = mask.data_ptr(), mask.numel() // cols
+    if row_len is not None:
+        if not row_len.is_cuda or row_len.dtype != torch.int32 or row_len.numel() != rows \
+                or not row_len.is_contiguous():
+            raise ValueError("row_len must be a contiguous int32 CUDA tensor with one entry per row")
+        len_ptr = row_len.data_ptr()
+    st = osm_softmax_rows_ex(x.data_ptr(), out.data_ptr(), rows, cols, code, mask_ptr, mask_rows,
+                             len_ptr, _stream_handle(x.device))
     if st != OSM_OK:
-        raise OsmError(st, "osm_softmax_rows")
+        raise OsmError(st, "osm_softmax_rows_ex")
     return out
 
 
-def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
+def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None, bias=None):
     """Fused attention forward on contiguous bfloat16 [B, H, N, D] CUDA tensors.
 
     Returns ``(o, lse)``: o is bfloat16 [B, H, N, D], lse float32 [B, H, N].
-    ``scale`` multiplies q.k and defaults to 1/sqrt(D).
+    ``scale`` multiplies q.k and defaults to 1/sqrt(D).  ``kv_len`` (int32
+    CUDA tensor [B]) hides keys past each batch's length; ``bias`` (float32
+    CUDA tensor broadcastable to [B, H, N, N], last two dims contiguous) is
+    added to the scaled scores.
     """
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -165,8 +207,22 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
-    st = osm_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                      B, H, N, D, float(scale), bool(causal), _stream_handle(q.device))
+    len_ptr, bias_ptr, sb, sh = 0, 0, 0, 0
+    if kv_len is not None:
+        if not kv_len.is_cuda or kv_len.dtype != torch.int32 or kv_len.numel() != B \
+                or not kv_len.is_contiguous():
+            raise ValueError("kv_len must be a contiguous int32 CUDA tensor of length B")
+        len_ptr = kv_len.data_ptr()
+    if bias is not None:
+        if not bias.is_cuda or bias.dtype != torch.float32 or bias.dim() != 4:
+            raise ValueError("bias must be a float32 CUDA tensor [B or 1, H or 1, N, N]")
+        bb = bias.expand(B, H, N, N)
+        if bb.stride(3) != 1 or bb.stride(2) != N:
+            raise ValueError("bias must have contiguous [N, N] trailing dims")
+        bias_ptr, sb, sh = bb.data_ptr(), bb.stride(0), bb.stride(1)
+    st = osm_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr(), B, H, N, D, float(scale), bool(causal), len_ptr,
+                         bias_ptr, sb, sh, _stream_handle(q.device))
     if st != OSM_OK:
-        raise OsmError(st, "osm_attn_fwd")
+        raise OsmError(st, "osm_attn_fwd_ex")
     return out, lse

@@ -191,10 +191,48 @@ __device__ __forceinline__ void compute_scores(const char* kbuf, const LaneOffse
 // One key tile j for one wavefront: mask and softmax the scores S_j held in
 // `scur`, then O^T += V_j^T P_j^T; with kNext, then form the scores of tile
 // j + 1 into `snext`, so 32 matrix products run back to back per tile.
-template <int D, bool kCausal, bool kNext>
+// Optional fused inputs: per-batch key lengths (keys at or past kv_len are
+// hidden) and an additive fp32 bias on the scaled scores, element (b, h, i, j)
+// at bias[b * stride_b + h * stride_h + i * N + j].
+struct AttnOptions {
+  const int32_t* kv_len;
+  const float* bias;
+  int64_t bias_stride_b, bias_stride_h;
+  float inv_scale;  // the bias enters the raw scores as bias / scale
+  bool bias_vec;    // N, strides and base allow 16-byte bias loads
+};
+
+// Add the bias of this lane's query row to its 32 raw scores of tile k0.
+__device__ __forceinline__ void add_bias(f32x16 (&s)[2], const float* brow, int k0, int half,
+                                         int N, const AttnOptions& opt) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int key = k0 + kb * 32 + g * 8 + half * 4;  // 4 consecutive keys
+      float b4[4];
+      if (opt.bias_vec) {
+        if (key < N) {
+          const float4 f = *reinterpret_cast<const float4*>(brow + key);
+          b4[0] = f.x; b4[1] = f.y; b4[2] = f.z; b4[3] = f.w;
+        } else {
+          b4[0] = b4[1] = b4[2] = b4[3] = 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b4[t] = key + t < N ? brow[key + t] : 0.0f;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s[kb][g * 4 + t] += b4[t] * opt.inv_scale;
+    }
+  }
+}
+
+template <int D, bool kCausal, bool kNext, bool kBias>
 __device__ __forceinline__ void tile_step(const char* kbuf_next, const char* vbuf,
-                                          const LaneOffsets<D>& off, int j, int N, int qw,
-                                          int qrow, int half, float scale_log2,
+                                          const LaneOffsets<D>& off, int j, int N, int kvlen,
+                                          int qw, int qrow, int half, float scale_log2,
+                                          const float* brow, const AttnOptions& opt,
                                           const bf16x8 (&qreg)[D / 16], f32x16 (&scur)[2],
                                           f32x16 (&snext)[2], f32x16 (&oacc)[D / 32],
                                           float& m_run, float& l_run) {
@@ -203,12 +241,15 @@ __device__ __forceinline__ void tile_step(const char* kbuf_next, const char* vbu
   constexpr int kRow = D * 2;  // bytes per key row
   const int k0 = j * kBN;
 
-  // A4: hide keys past the causal diagonal or past the end of the sequence.
-  const bool need_mask = (kCausal && k0 + kBN - 1 > qw) || (k0 + kBN > N);
+  if constexpr (kBias) {
+    if (qrow < N) add_bias(scur, brow, k0, half, N, opt);
+  }
+  // A4: hide keys past the causal diagonal or past the valid keys.
+  const bool need_mask = (kCausal && k0 + kBN - 1 > qw) || (k0 + kBN > kvlen);
   if (need_mask) {
     // Keys k0 + (i / 4) * 8 + half * 4 + i % 4 (+ 32) are visible when below
     // lim; compare the constant part against lim - k0 - 4 * half.
-    const int lim = (kCausal ? min(N, qrow + 1) : N) - k0 - half * 4;
+    const int lim = (kCausal ? min(kvlen, qrow + 1) : kvlen) - k0 - half * 4;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kk = (i >> 2) * 8 + (i & 3);
@@ -275,11 +316,11 @@ __device__ __forceinline__ void tile_step(const char* kbuf_next, const char* vbu
   if constexpr (kNext) compute_scores<D>(kbuf_next, off, qreg, snext);
 }
 
-template <int D, bool kCausal>
+template <int D, bool kCausal, bool kBias>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int BH,
-    int N, float scale_log2) {
+    int H, int N, float scale_log2, AttnOptions opt) {
   using T = Tile<D>;
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
@@ -307,11 +348,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int q0 = qt * kBM;
   const int qw = q0 + wave * 32;  // first query row of this wave
   const int qrow = qw + col;      // this lane's query row
+  const int b = bh / H, h = bh % H;
+  const int kvlen = opt.kv_len ? min(max(opt.kv_len[b], 0), N) : N;
+  const float* brow = kBias ? opt.bias + b * opt.bias_stride_b + h * opt.bias_stride_h +
+                                  (int64_t)min(qrow, N - 1) * N
+                            : nullptr;
 
-  const int kv_end = kCausal ? min(N, q0 + kBM) : N;
+  const int kv_end = kCausal ? min(kvlen, q0 + kBM) : kvlen;
   const int ntiles = (kv_end + kBN - 1) / kBN;
   // Last key tile with work for this wave (-1: the wave is past the end).
-  const int jw_last = qw >= N ? -1 : (kCausal ? min(ntiles - 1, (qw + 31) / kBN) : ntiles - 1);
+  const int jw_last =
+      (qw >= N || ntiles == 0) ? -1 : (kCausal ? min(ntiles - 1, (qw + 31) / kBN) : ntiles - 1);
 
   // A2 prologue: K_0, V_0 and K_1 in flight.
   issue_tile<D, T::k_swz>(kbuf0, kh, head_bytes, 0, wave, lane);
@@ -347,11 +394,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     if (j + 2 < ntiles) issue_tile<D, T::k_swz>(kbuf0, kh, head_bytes, (j + 2) * kBN, wave, lane);
     if (j + 1 < ntiles) issue_tile<D, T::v_swz>(vbuf1, vh, head_bytes, (j + 1) * kBN, wave, lane);
     if (j < jw_last) {
-      tile_step<D, kCausal, true>(kbuf1, vbuf0, off, j, N, qw, qrow, half, scale_log2, qreg, sA,
-                                  sB, oacc, m_run, l_run);
+      tile_step<D, kCausal, true, kBias>(kbuf1, vbuf0, off, j, N, kvlen, qw, qrow, half,
+                                         scale_log2, brow, opt, qreg, sA, sB, oacc, m_run, l_run);
     } else if (j == jw_last) {
-      tile_step<D, kCausal, false>(kbuf1, vbuf0, off, j, N, qw, qrow, half, scale_log2, qreg, sA,
-                                   sB, oacc, m_run, l_run);
+      tile_step<D, kCausal, false, kBias>(kbuf1, vbuf0, off, j, N, kvlen, qw, qrow, half,
+                                          scale_log2, brow, opt, qreg, sA, sB, oacc, m_run, l_run);
     }
     if (j + 1 >= ntiles) break;
     __builtin_amdgcn_s_waitcnt(0);
@@ -359,11 +406,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     if (j + 3 < ntiles) issue_tile<D, T::k_swz>(kbuf1, kh, head_bytes, (j + 3) * kBN, wave, lane);
     if (j + 2 < ntiles) issue_tile<D, T::v_swz>(vbuf0, vh, head_bytes, (j + 2) * kBN, wave, lane);
     if (j + 1 < jw_last) {
-      tile_step<D, kCausal, true>(kbuf0, vbuf1, off, j + 1, N, qw, qrow, half, scale_log2, qreg,
-                                  sB, sA, oacc, m_run, l_run);
+      tile_step<D, kCausal, true, kBias>(kbuf0, vbuf1, off, j + 1, N, kvlen, qw, qrow, half,
+                                         scale_log2, brow, opt, qreg, sB, sA, oacc, m_run, l_run);
     } else if (j + 1 == jw_last) {
-      tile_step<D, kCausal, false>(kbuf0, vbuf1, off, j + 1, N, qw, qrow, half, scale_log2, qreg,
-                                   sB, sA, oacc, m_run, l_run);
+      tile_step<D, kCausal, false, kBias>(kbuf0, vbuf1, off, j + 1, N, kvlen, qw, qrow, half,
+                                          scale_log2, brow, opt, qreg, sB, sA, oacc, m_run, l_run);
     }
   }
 
@@ -390,30 +437,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   }
 }
 
-template <int D, bool kCausal>
-hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                  float scale, hipStream_t s) {
+template <int D, bool kCausal, bool kBias>
+hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int H,
+                  int N, float scale, const AttnOptions& opt, hipStream_t s) {
   const int nqt = (N + kBM - 1) / kBM;
   const float scale_log2 = scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, kCausal>), dim3(nqt * BH), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, kCausal, kBias>), dim3(nqt * BH), dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, N,
-                     scale_log2);
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, H, N,
+                     scale_log2, opt);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                    int H, int N, float scale, bool causal, const AttnOptions& opt,
+                    hipStream_t s) {
+  if (opt.bias != nullptr) {
+    return causal ? launch<D, true, true>(q, k, v, o, lse, BH, H, N, scale, opt, s)
+                  : launch<D, false, true>(q, k, v, o, lse, BH, H, N, scale, opt, s);
+  }
+  return causal ? launch<D, true, false>(q, k, v, o, lse, BH, H, N, scale, opt, s)
+                : launch<D, false, false>(q, k, v, o, lse, BH, H, N, scale, opt, s);
 }
 
 }  // namespace
 
 hipError_t attn_fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int D, float scale, bool causal,
-                           hipStream_t stream) {
+                           const int32_t* kv_len, const float* bias, int64_t bias_stride_b,
+                           int64_t bias_stride_h, hipStream_t stream) {
   const int BH = B * H;
-  if (D == 64) {
-    return causal ? launch<64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch<64, false>(q, k, v, o, lse, BH, N, scale, stream);
-  }
-  return causal ? launch<128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch<128, false>(q, k, v, o, lse, BH, N, scale, stream);
+  AttnOptions opt;
+  opt.kv_len = kv_len;
+  opt.bias = bias;
+  opt.bias_stride_b = bias_stride_b;
+  opt.bias_stride_h = bias_stride_h;
+  opt.inv_scale = 1.0f / scale;
+  opt.bias_vec = bias != nullptr && (N % 4) == 0 && (bias_stride_b % 4) == 0 &&
+                 (bias_stride_h % 4) == 0 && (reinterpret_cast<uintptr_t>(bias) % 16) == 0;
+  if (D == 64) return launch_d<64>(q, k, v, o, lse, BH, H, N, scale, causal, opt, stream);
+  return launch_d<128>(q, k, v, o, lse, BH, H, N, scale, causal, opt, stream);
 }
 
 }  // namespace osm

@@ -30,23 +30,36 @@ const char* osm_status_string(int status) {
 
 const char* osm_version(void) { return "0.1.0"; }
 
-int osm_softmax_rows(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
-                     void* stream) {
+int osm_softmax_rows_ex(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                        const void* mask, int64_t mask_rows, const int32_t* row_len,
+                        void* stream) {
   if (dtype != OSM_F32 && dtype != OSM_BF16) return OSM_ERR_INVALID_ARG;
   if (rows < 0 || cols < 0 || cols > INT32_MAX) return OSM_ERR_INVALID_ARG;
+  if (mask != nullptr && mask_rows < 1) return OSM_ERR_INVALID_ARG;
   if (rows == 0 || cols == 0) return OSM_OK;
   if (in == nullptr || out == nullptr) return OSM_ERR_INVALID_ARG;
   const int64_t esize = dtype == OSM_F32 ? 4 : 2;
   if (rows > INT64_MAX / cols / esize) return OSM_ERR_INVALID_ARG;
+  if (mask != nullptr && mask_rows > INT64_MAX / cols / esize) return OSM_ERR_INVALID_ARG;
   if (!aligned(in, esize) || !aligned(out, esize)) return OSM_ERR_INVALID_ARG;
+  if (mask != nullptr && !aligned(mask, esize)) return OSM_ERR_INVALID_ARG;
+  if (row_len != nullptr && !aligned(row_len, 4)) return OSM_ERR_INVALID_ARG;
   const int64_t vec = 16 / esize;
-  const bool vector_path = aligned(in, 16) && aligned(out, 16) && (cols % vec) == 0;
-  return from_hip(osm::softmax_rows_launch(in, out, rows, (int)cols, dtype, vector_path,
-                                           static_cast<hipStream_t>(stream)));
+  const bool vector_path = aligned(in, 16) && aligned(out, 16) && (cols % vec) == 0 &&
+                           (mask == nullptr || aligned(mask, 16));
+  return from_hip(osm::softmax_rows_launch(in, out, rows, (int)cols, dtype, vector_path, mask,
+                                           mask_rows, row_len, static_cast<hipStream_t>(stream)));
 }
 
-int osm_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                 int N, int D, float scale, int causal, void* stream) {
+int osm_softmax_rows(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                     void* stream) {
+  return osm_softmax_rows_ex(in, out, rows, cols, dtype, nullptr, 0, nullptr, stream);
+}
+
+int osm_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int N, int D, float scale, int causal, const int32_t* kv_len,
+                    const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                    void* stream) {
   if (B < 0 || H < 0 || N < 0 || D < 0) return OSM_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || !isfinite(scale)) return OSM_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return OSM_ERR_UNSUPPORTED;
@@ -59,14 +72,25 @@ int osm_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4))
     return OSM_ERR_INVALID_ARG;
-  // One 256-thread workgroup per 128 query rows of each (batch, head): the
-  // launch must stay below 2^32 work-items.
+  if (kv_len != nullptr && !aligned(kv_len, 4)) return OSM_ERR_INVALID_ARG;
+  if (bias != nullptr) {
+    if (!aligned(bias, 4) || bias_stride_b < 0 || bias_stride_h < 0) return OSM_ERR_INVALID_ARG;
+  }
   // Key/value tiles are addressed with 32-bit buffer offsets within one head.
   if (((int64_t)N + 64) * D * 2 >= ((int64_t)1 << 31)) return OSM_ERR_UNSUPPORTED;
+  // One 256-thread workgroup per 128 query rows of each (batch, head): the
+  // launch must stay below 2^32 work-items.
   const int64_t workgroups = bh * (((int64_t)N + 127) / 128);
   if (workgroups * 256 >= ((int64_t)1 << 32)) return OSM_ERR_UNSUPPORTED;
-  return from_hip(osm::attn_fwd_launch(q, k, v, o, lse, B, H, N, D, scale, causal != 0,
+  return from_hip(osm::attn_fwd_launch(q, k, v, o, lse, B, H, N, D, scale, causal != 0, kv_len,
+                                       bias, bias_stride_b, bias_stride_h,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int osm_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int D, float scale, int causal, void* stream) {
+  return osm_attn_fwd_ex(q, k, v, o, lse, B, H, N, D, scale, causal, nullptr, nullptr, 0, 0,
+                         stream);
 }
 
 }  // extern "C"

@@ -7,15 +7,21 @@
 
 namespace osm {
 
-// Row softmax.  dtype 0 = float32, 1 = bfloat16.  `vector_path` requires both
-// pointers 16-byte aligned and cols a multiple of the 16-byte vector.
+// Row softmax.  dtype 0 = float32, 1 = bfloat16.  `vector_path` requires all
+// pointers 16-byte aligned and cols a multiple of the 16-byte vector.  `mask`
+// (nullable, input dtype, [mask_rows, cols]) is added to the input; `row_len`
+// (nullable, int32 [rows]) limits each row.
 hipError_t softmax_rows_launch(const void* in, void* out, int64_t rows, int cols, int dtype,
-                               bool vector_path, hipStream_t stream);
+                               bool vector_path, const void* mask, int64_t mask_rows,
+                               const int32_t* row_len, hipStream_t stream);
 
 // Fused attention forward, bfloat16 [B, H, N, D] in/out, float32 LSE [B, H, N].
-// D must be 64 or 128.
+// D must be 64 or 128.  kv_len (nullable, int32 [B]) limits the keys of each
+// batch; bias (nullable, fp32) is added to the scaled scores, element
+// (b, h, i, j) at bias[b * bias_stride_b + h * bias_stride_h + i * N + j].
 hipError_t attn_fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int D, float scale, bool causal,
-                           hipStream_t stream);
+                           const int32_t* kv_len, const float* bias, int64_t bias_stride_b,
+                           int64_t bias_stride_h, hipStream_t stream);
 
 }  // namespace osm

@@ -34,7 +34,6 @@ struct Elem;
 
 template <>
 struct Elem<float> {
-  static constexpr int kVec = 4;  // floats per 16-byte vector
   __device__ static void unpack(const u32x4& w, float* f) {
     f[0] = __uint_as_float(w[0]);
     f[1] = __uint_as_float(w[1]);
@@ -55,7 +54,6 @@ struct Bf16 {};  // tag: bfloat16 storage
 
 template <>
 struct Elem<Bf16> {
-  static constexpr int kVec = 8;  // bfloat16 per 16-byte vector
   __device__ static void unpack(const u32x4& w, float* f) {
     f[0] = bf16_lo(w[0]); f[1] = bf16_hi(w[0]);
     f[2] = bf16_lo(w[1]); f[3] = bf16_hi(w[1]);
@@ -85,6 +83,45 @@ __device__ __forceinline__ float tree_sum(const float* v) {
   }
 }
 
+// Optional fused inputs ([Ch6 §6.7.3]): an additive mask of the input dtype,
+// row r using mask row r % mask_rows, and per-row lengths (entries at or past
+// len[r] count as -inf).  Both pointers may be null.
+struct RowOptions {
+  const void* mask;
+  int64_t mask_rows;
+  const int32_t* lens;
+  __device__ int length(int64_t row, int cols) const {
+    if (lens == nullptr) return cols;
+    const int n = lens[row];
+    return n < 0 ? 0 : (n > cols ? cols : n);
+  }
+};
+
+// Load one vector (or scalar) of a row with the mask added and the length
+// applied.
+template <typename E, int VEC>
+__device__ __forceinline__ void load_masked(const void* in, int64_t base, int64_t mbase, int v,
+                                            int len, const RowOptions& opt, float* x) {
+  if constexpr (VEC == 1) {
+    x[0] = E::load1(in, base + v);
+    if (opt.mask) x[0] += E::load1(opt.mask, mbase + v);
+  } else {
+    E::unpack(*reinterpret_cast<const u32x4*>(static_cast<const char*>(in) +
+                                               (base + (int64_t)v * VEC) * (16 / VEC)),
+              x);
+    if (opt.mask) {
+      float mv[VEC];
+      E::unpack(*reinterpret_cast<const u32x4*>(static_cast<const char*>(opt.mask) +
+                                                 (mbase + (int64_t)v * VEC) * (16 / VEC)),
+                mv);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) x[j] += mv[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) x[j] = v * VEC + j < len ? x[j] : kNegInf;
+}
+
 // Merge the per-wave states of one row through LDS.  `slot` holds one (m, l)
 // per wave of the row; every lane reads all of them and folds them in wave
 // order, so the result is identical on every lane and on every run.
@@ -105,9 +142,9 @@ __device__ __forceinline__ void lds_combine(float& m, float& l, float2* slot, in
 // Resident kernel.  T threads per row (a multiple of 64), NV vectors of VEC
 // elements per lane (VEC = 1 is the scalar path for unaligned inputs).  A
 // 256-thread workgroup serves 256 / T rows (or one row when T >= 256).
-template <typename E, int VEC, int NV, int T>
+template <typename E, int VEC, int NV, int T, bool kOpt>
 __global__ __launch_bounds__(T >= 256 ? T : 256) void softmax_resident_kernel(
-    const void* in, void* out, int64_t rows, int cols) {
+    const void* in, void* out, int64_t rows, int cols, RowOptions opt) {
   constexpr int kBlock = T >= 256 ? T : 256;
   constexpr int kRowsPerBlock = kBlock / T;
   constexpr int kWavesPerRow = T / 64;
@@ -126,6 +163,8 @@ __global__ __launch_bounds__(T >= 256 ? T : 256) void softmax_resident_kernel(
     const int64_t row = row0 + row_in_block;
     const bool live_row = row < rows;
     const int64_t base = row * (int64_t)cols;
+    const int len = kOpt ? (live_row ? opt.length(row, cols) : 0) : cols;
+    const int64_t mbase = kOpt && opt.mask ? (row % opt.mask_rows) * (int64_t)cols : 0;
 
     // R1: load the row into registers; missing elements take the identity -inf.
     float x[kN];
@@ -135,11 +174,26 @@ __global__ __launch_bounds__(T >= 256 ? T : 256) void softmax_resident_kernel(
       if (live_row && v < vcols) {
         if constexpr (VEC == 1) {
           x[k] = E::load1(in, base + v);
+          if (kOpt && opt.mask) x[k] += E::load1(opt.mask, mbase + v);
         } else {
           const u32x4 w = __builtin_nontemporal_load(
               reinterpret_cast<const u32x4*>(static_cast<const char*>(in) +
                                              (base + (int64_t)v * VEC) * (16 / VEC)));
           E::unpack(w, &x[k * VEC]);
+          if (kOpt && opt.mask) {
+            float mv[VEC];
+            E::unpack(*reinterpret_cast<const u32x4*>(static_cast<const char*>(opt.mask) +
+                                                      (mbase + (int64_t)v * VEC) * (16 / VEC)),
+                      mv);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) x[k * VEC + j] += mv[j];
+          }
+        }
+        // Entries past the row's length take part as -inf (output 0).
+        if constexpr (kOpt) {
+#pragma unroll
+          for (int j = 0; j < VEC; ++j)
+            x[k * VEC + j] = v * VEC + j < len ? x[k * VEC + j] : kNegInf;
         }
       } else {
 #pragma unroll
@@ -190,7 +244,8 @@ __global__ __launch_bounds__(T >= 256 ? T : 256) void softmax_resident_kernel(
 // second pass that re-reads the row and writes exp(x - m) / l.
 template <typename E, int VEC>
 __global__ __launch_bounds__(1024) void softmax_looping_kernel(const void* in, void* out,
-                                                                int64_t rows, int cols) {
+                                                                int64_t rows, int cols,
+                                                                RowOptions opt) {
   constexpr int T = 1024;
   __shared__ float2 slots[2][T / 64];
   const int t = threadIdx.x;
@@ -198,16 +253,12 @@ __global__ __launch_bounds__(1024) void softmax_looping_kernel(const void* in, v
   int parity = 0;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x, parity ^= 1) {
     const int64_t base = row * (int64_t)cols;
+    const int len = opt.length(row, cols);
+    const int64_t mbase = opt.mask ? (row % opt.mask_rows) * (int64_t)cols : 0;
     float m = kNegInf, l = 0.0f;
     for (int v = t; v < vcols; v += T) {
       float x[VEC];
-      if constexpr (VEC == 1) {
-        x[0] = E::load1(in, base + v);
-      } else {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const char*>(in) +
-                                                         (base + (int64_t)v * VEC) * (16 / VEC));
-        E::unpack(w, x);
-      }
+      load_masked<E, VEC>(in, base, mbase, v, len, opt, x);
       float mv = kNegInf;
 #pragma unroll
       for (int j = 0; j < VEC; ++j) mv = fmaxf(mv, x[j]);
@@ -225,13 +276,7 @@ __global__ __launch_bounds__(1024) void softmax_looping_kernel(const void* in, v
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     for (int v = t; v < vcols; v += T) {
       float x[VEC];
-      if constexpr (VEC == 1) {
-        x[0] = E::load1(in, base + v);
-      } else {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const char*>(in) +
-                                                         (base + (int64_t)v * VEC) * (16 / VEC));
-        E::unpack(w, x);
-      }
+      load_masked<E, VEC>(in, base, mbase, v, len, opt, x);
 #pragma unroll
       for (int j = 0; j < VEC; ++j) x[j] = exp2_hw((x[j] - r) * kLog2e) * inv;
       if constexpr (VEC == 1) {
@@ -256,12 +301,18 @@ inline unsigned grid_for(int64_t row_groups) {
 }
 
 template <typename E, int VEC, int NV, int T>
-hipError_t launch_resident(const void* in, void* out, int64_t rows, int cols, hipStream_t s) {
+hipError_t launch_resident(const void* in, void* out, int64_t rows, int cols,
+                           const RowOptions& opt, hipStream_t s) {
   constexpr int kBlock = T >= 256 ? T : 256;
   constexpr int kRowsPerBlock = kBlock / T;
   const int64_t groups = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL((softmax_resident_kernel<E, VEC, NV, T>), dim3(grid_for(groups)),
-                     dim3(kBlock), 0, s, in, out, rows, cols);
+  if (opt.mask != nullptr || opt.lens != nullptr) {
+    hipLaunchKernelGGL((softmax_resident_kernel<E, VEC, NV, T, true>), dim3(grid_for(groups)),
+                       dim3(kBlock), 0, s, in, out, rows, cols, opt);
+  } else {
+    hipLaunchKernelGGL((softmax_resident_kernel<E, VEC, NV, T, false>), dim3(grid_for(groups)),
+                       dim3(kBlock), 0, s, in, out, rows, cols, opt);
+  }
   return hipGetLastError();
 }
 
@@ -270,35 +321,38 @@ hipError_t launch_resident(const void* in, void* out, int64_t rows, int cols, hi
 // threads for long rows, at most 64 values per lane (so that 1024-thread
 // workgroups fit in 128 VGPRs); otherwise the looping kernel.
 template <typename E, int VEC>
-hipError_t dispatch(const void* in, void* out, int64_t rows, int cols, hipStream_t s) {
+hipError_t dispatch(const void* in, void* out, int64_t rows, int cols, const RowOptions& opt,
+                    hipStream_t s) {
   constexpr int kMaxNV = (64 / VEC) < 16 ? (64 / VEC) : 16;
   const int nvec = cols / VEC;
-  if (nvec <= 64 * 1) return launch_resident<E, VEC, 1, 64>(in, out, rows, cols, s);
-  if (nvec <= 64 * 2) return launch_resident<E, VEC, 2, 64>(in, out, rows, cols, s);
-  if (nvec <= 64 * 4) return launch_resident<E, VEC, 4, 64>(in, out, rows, cols, s);
+  if (nvec <= 64 * 1) return launch_resident<E, VEC, 1, 64>(in, out, rows, cols, opt, s);
+  if (nvec <= 64 * 2) return launch_resident<E, VEC, 2, 64>(in, out, rows, cols, opt, s);
+  if (nvec <= 64 * 4) return launch_resident<E, VEC, 4, 64>(in, out, rows, cols, opt, s);
   if constexpr (kMaxNV >= 8) {
-    if (nvec <= 64 * 8) return launch_resident<E, VEC, 8, 64>(in, out, rows, cols, s);
+    if (nvec <= 64 * 8) return launch_resident<E, VEC, 8, 64>(in, out, rows, cols, opt, s);
   }
-  if (nvec <= 256 * 4) return launch_resident<E, VEC, 4, 256>(in, out, rows, cols, s);
+  if (nvec <= 256 * 4) return launch_resident<E, VEC, 4, 256>(in, out, rows, cols, opt, s);
   if (nvec <= 256 * kMaxNV / 2 && kMaxNV / 2 > 4)
-    return launch_resident<E, VEC, kMaxNV / 2 < 4 ? 4 : kMaxNV / 2, 256>(in, out, rows, cols, s);
-  if (nvec <= 256 * kMaxNV) return launch_resident<E, VEC, kMaxNV, 256>(in, out, rows, cols, s);
-  if (nvec <= 1024 * kMaxNV) return launch_resident<E, VEC, kMaxNV, 1024>(in, out, rows, cols, s);
+    return launch_resident<E, VEC, kMaxNV / 2 < 4 ? 4 : kMaxNV / 2, 256>(in, out, rows, cols, opt, s);
+  if (nvec <= 256 * kMaxNV) return launch_resident<E, VEC, kMaxNV, 256>(in, out, rows, cols, opt, s);
+  if (nvec <= 1024 * kMaxNV) return launch_resident<E, VEC, kMaxNV, 1024>(in, out, rows, cols, opt, s);
   hipLaunchKernelGGL((softmax_looping_kernel<E, VEC>), dim3(grid_for(rows)), dim3(1024), 0, s, in,
-                     out, rows, cols);
+                     out, rows, cols, opt);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t softmax_rows_launch(const void* in, void* out, int64_t rows, int cols, int dtype,
-                               bool vector_path, hipStream_t s) {
+                               bool vector_path, const void* mask, int64_t mask_rows,
+                               const int32_t* row_len, hipStream_t s) {
+  const RowOptions opt{mask, mask_rows > 0 ? mask_rows : 1, row_len};
   if (dtype == 0) {
-    return vector_path ? dispatch<Elem<float>, 4>(in, out, rows, cols, s)
-                       : dispatch<Elem<float>, 1>(in, out, rows, cols, s);
+    return vector_path ? dispatch<Elem<float>, 4>(in, out, rows, cols, opt, s)
+                       : dispatch<Elem<float>, 1>(in, out, rows, cols, opt, s);
   }
-  return vector_path ? dispatch<Elem<Bf16>, 8>(in, out, rows, cols, s)
-                     : dispatch<Elem<Bf16>, 1>(in, out, rows, cols, s);
+  return vector_path ? dispatch<Elem<Bf16>, 8>(in, out, rows, cols, opt, s)
+                     : dispatch<Elem<Bf16>, 1>(in, out, rows, cols, opt, s);
 }
 
 }  // namespace osm

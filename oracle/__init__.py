@@ -16,8 +16,9 @@ the source pages:
 
 Modules
 -------
-softmax_ref    three-pass safe softmax ([Ch6 §6.2]) and the unsafe two-pass
-               form ([Ch6 §6.1]) kept as a negative control.
+softmax_ref    three-pass safe softmax ([Ch6 §6.2]), its fused additive-mask /
+               row-length form ([Ch6 §6.7.3]), and the unsafe two-pass form
+               ([Ch6 §6.1]) kept as a negative control.
 online_ref     the element-wise online normaliser and the (m, l) combine
                ([Ch6 §6.3.1], [Ch6 §6.4.1]); used only to check the oracle
                itself (online == two-pass by brute force).
@@ -30,12 +31,13 @@ tie it to something other than itself live in ``tests/test_oracle_*.py``.
 Parity status of each function is stated in its docstring.
 """
 
-from .softmax_ref import softmax_rows_ref, naive_softmax_rows_f32
+from .softmax_ref import masked_softmax_rows_ref, naive_softmax_rows_f32, softmax_rows_ref
 from .online_ref import EMPTY_STATE, all_trees, combine, online_state, tree_reduce
 from .attention_ref import attention_head_ref, attention_ref, blocked_attention_row_ref
 
 __all__ = [
     "softmax_rows_ref",
+    "masked_softmax_rows_ref",
     "naive_softmax_rows_f32",
     "EMPTY_STATE",
     "combine",

@@ -22,7 +22,8 @@ def _scale64(scale):
     return float(np.float32(scale))
 
 
-def attention_head_ref(q, k, v, scale, causal, query_rows=None, chunk=512):
+def attention_head_ref(q, k, v, scale, causal, query_rows=None, chunk=512, kv_len=None,
+                       bias=None):
     """Attention for one (batch, head) slice, float64.
 
     The definition of [xxqk §4.2] and [Ch6 §6.6] ("naive attention"):
@@ -42,6 +43,10 @@ def attention_head_ref(q, k, v, scale, causal, query_rows=None, chunk=512):
     scale : float, a multiplier (taken at float32 precision).
     causal : bool.  Query row i may see keys 0..i (same-length Q and K).
     query_rows : optional iterable of absolute query indices to compute.
+    kv_len : optional number of valid keys; keys at or past it are hidden
+        (key padding, an additive -inf mask on those columns, [xxqk §6.3]).
+    bias : optional (Nq, Nk) additive term on the scaled scores, S = scale *
+        q.k + bias ([Ch6 §6.7.3]'s fused additive mask, applied to scores).
 
     Returns
     -------
@@ -63,6 +68,10 @@ def attention_head_ref(q, k, v, scale, causal, query_rows=None, chunk=512):
     for c0 in range(0, len(rows), chunk):
         r = rows[c0:c0 + chunk]
         S = s64 * (q[r] @ k.T)                       # (rows, Nk)
+        if bias is not None:
+            S = S + np.asarray(bias, dtype=np.float64)[r]
+        if kv_len is not None:
+            S = np.where(key_idx[None, :] >= int(kv_len), -np.inf, S)
         if causal:
             S = np.where(key_idx[None, :] > r[:, None], -np.inf, S)
         m = np.max(S, axis=1)                         # pass 1
@@ -78,10 +87,12 @@ def attention_head_ref(q, k, v, scale, causal, query_rows=None, chunk=512):
     return out, lse
 
 
-def attention_ref(q, k, v, scale, causal, heads=None, chunk=512):
+def attention_ref(q, k, v, scale, causal, heads=None, chunk=512, kv_len=None, bias=None):
     """Attention over [B, H, N, D] tensors, float64.
 
-    ``heads`` selects (b, h) slices; by default all of them.  Returns
+    ``heads`` selects (b, h) slices; by default all of them.  ``kv_len`` is an
+    optional per-batch count of valid keys (length B); ``bias`` an optional
+    additive term broadcastable to [B, H, N, N].  Returns
     ``O`` of shape (len(heads), N, D) and ``LSE`` of shape (len(heads), N) when
     ``heads`` is given, else (B, H, N, D) and (B, H, N).
     """
@@ -92,8 +103,13 @@ def attention_ref(q, k, v, scale, causal, heads=None, chunk=512):
     sel = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     O = np.zeros((len(sel), N, v.shape[3]))
     L = np.zeros((len(sel), N))
+    bias_full = None if bias is None else np.broadcast_to(np.asarray(bias, dtype=np.float64),
+                                                          (B, H, N, N))
     for i, (b, h) in enumerate(sel):
-        O[i], L[i] = attention_head_ref(q[b, h], k[b, h], v[b, h], scale, causal, chunk=chunk)
+        O[i], L[i] = attention_head_ref(
+            q[b, h], k[b, h], v[b, h], scale, causal, chunk=chunk,
+            kv_len=None if kv_len is None else int(kv_len[b]),
+            bias=None if bias_full is None else bias_full[b, h])
     if heads is None:
         return O.reshape(B, H, N, v.shape[3]), L.reshape(B, H, N)
     return O, L

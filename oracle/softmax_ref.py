@@ -68,6 +68,34 @@ def softmax_rows_ref(x, return_stats=False):
     return y, (m_out, s_out, lse)
 
 
+def masked_softmax_rows_ref(x, mask=None, row_len=None):
+    """Softmax of ``x + mask`` with per-row lengths, float64.
+
+    The fused additive mask of [Ch6 §6.7.3]: each logit becomes
+    ``x[r, i] + mask[r % mask_rows, i]`` (a mask of 0 / -inf hides entries, any
+    finite value biases them).  With ``row_len``, only the first
+    ``row_len[r]`` entries of row r take part (lengths are clamped to
+    [0, cols]); the remaining outputs are 0, as for -inf logits.  Then the
+    three-pass safe softmax of ``softmax_rows_ref`` is applied.
+
+    Parity status: pinned (tests: a zero mask and full lengths give the
+    unmasked result; a -inf mask equals writing -inf into x; a length equals
+    truncating the row and zero-padding; broadcast masks equal tiled masks).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    z = x.copy()
+    if mask is not None:
+        m = np.asarray(mask, dtype=np.float64)
+        if m.ndim == 1:
+            m = m[None, :]
+        z = z + m[np.arange(rows) % m.shape[0]]
+    if row_len is not None:
+        lens = np.clip(np.asarray(row_len, dtype=np.int64), 0, cols)
+        z = np.where(np.arange(cols)[None, :] < lens[:, None], z, -np.inf)
+    return softmax_rows_ref(z)
+
+
 def naive_softmax_rows_f32(x):
     """The unsafe two-pass softmax of [Ch6 §6.1], evaluated in float32.
 

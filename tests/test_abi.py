@@ -31,8 +31,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["osm_attn_fwd", "osm_softmax_rows", "osm_status_string",
-                                     "osm_version"]
+    assert _declared_functions() == ["osm_attn_fwd", "osm_attn_fwd_ex", "osm_softmax_rows",
+                                     "osm_softmax_rows_ex", "osm_status_string", "osm_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -107,3 +107,28 @@ def test_tensor_helpers_reject_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         osm.attn_fwd(x, x, x)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((FAKE, FAKE, 4, 8, 0, FAKE, 0, 0), osm.OSM_ERR_INVALID_ARG),      # mask_rows < 1
+    ((FAKE, FAKE, 4, 8, 0, FAKE + 2, 1, 0), osm.OSM_ERR_INVALID_ARG),  # misaligned mask
+    ((FAKE, FAKE, 4, 8, 0, 0, 0, FAKE + 2), osm.OSM_ERR_INVALID_ARG),  # misaligned lengths
+    ((FAKE, FAKE, 4, 8, 5, 0, 0, 0), osm.OSM_ERR_INVALID_ARG),         # unknown dtype
+    ((0, 0, 0, 8, 0, FAKE, 1, FAKE), osm.OSM_OK),                      # empty: no-op
+])
+def test_softmax_ex_argument_checks(lib, args, expect):
+    assert osm.osm_softmax_rows_ex(*args, 0) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(kv_len=FAKE + 2), osm.OSM_ERR_INVALID_ARG),
+    (dict(bias=FAKE + 2), osm.OSM_ERR_INVALID_ARG),
+    (dict(bias=FAKE, bias_stride_b=-1), osm.OSM_ERR_INVALID_ARG),
+    (dict(bias=FAKE, D=80), osm.OSM_ERR_UNSUPPORTED),
+    (dict(N=0, kv_len=FAKE + 2), osm.OSM_OK),
+])
+def test_attention_ex_argument_checks(lib, kw, expect):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, D=64, scale=0.125,
+             causal=0, kv_len=0, bias=0, bias_stride_b=0, bias_stride_h=0)
+    a.update(kw)
+    assert osm.osm_attn_fwd_ex(*a.values(), 0) == expect

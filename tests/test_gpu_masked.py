@@ -1,0 +1,176 @@
+"""GPU parity of the fused mask / row length / key padding / bias entry points.
+
+osm_softmax_rows_ex against the oracle's masked softmax, osm_attn_fwd_ex
+against the oracle's attention with key lengths and an additive bias.  The
+tolerances are those of the plain entry points: float32 softmax 1e-6 absolute,
+bfloat16 softmax one bfloat16 ulp, attention O 2e-2 and LSE 1e-3.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_06_amd as osm
+import osm_inputs
+from oracle import attention_ref, masked_softmax_rows_ref
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    osm.load_library()
+
+
+def _announce(*what):
+    print("[case]", *what, flush=True)
+
+
+def _ulp(y):
+    y = np.abs(y)
+    e = np.floor(np.log2(np.where(y > 0, y, 1.0)))
+    return np.maximum(np.exp2(e - 7), 2.0 ** -133)
+
+
+def _check_softmax(x, mask, lens, y, dtype):
+    ref = masked_softmax_rows_ref(x.double().numpy(),
+                                  None if mask is None else mask.double().numpy(),
+                                  None if lens is None else lens.numpy())
+    got = y.double().cpu().numpy()
+    assert not np.isnan(got).any()
+    assert (got[ref == 0] == 0).all(), "hidden entries must be exactly 0"
+    err = np.abs(got - ref)
+    if dtype == torch.float32:
+        assert err.max(initial=0) <= 1e-6, err.max()
+    else:
+        assert (err <= _ulp(ref)).all(), err.max()
+
+
+def _mask(rows, cols, kind, seed, dtype):
+    g = torch.Generator().manual_seed(seed)
+    if kind == "pad":   # 0 / -inf, as for key padding
+        m = torch.where(torch.rand(rows, cols, generator=g) < 0.2, float("-inf"), 0.0)
+    else:               # a finite additive bias
+        m = torch.randn(rows, cols, generator=g)
+    return m.to(dtype)
+
+
+SHAPES = [(7, 3), (9, 100), (5, 1000), (3, 8192), (2, 12289), (2, 70001)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("kind", ["pad", "bias"])
+def test_softmax_mask_and_lengths(rows, cols, dtype, kind):
+    _announce("softmax_ex", rows, cols, dtype, kind)
+    x = osm_inputs.softmax_rows(rows, cols, seed=rows + cols, sigma=2.0, ninf_prob=0.0,
+                                dtype=dtype)
+    g = torch.Generator().manual_seed(cols)
+    lens = torch.randint(-2, cols + 3, (rows,), generator=g, dtype=torch.int32)
+    lens[0] = cols
+    for mask_rows in (rows, 1, 3):
+        mask = _mask(mask_rows, cols, kind, mask_rows + cols, dtype)
+        for use_len in (False, True):
+            ln = lens if use_len else None
+            y = osm.softmax_rows(x.cuda(), mask=mask.cuda(),
+                                 row_len=None if ln is None else ln.cuda())
+            torch.cuda.synchronize()
+            _check_softmax(x, mask, ln, y, dtype)
+    # lengths alone
+    y = osm.softmax_rows(x.cuda(), row_len=lens.cuda())
+    torch.cuda.synchronize()
+    _check_softmax(x, None, lens, y, dtype)
+
+
+def test_softmax_mask_scalar_path():
+    # Shifting every pointer by one element forces the scalar path.
+    rows, cols = 6, 1024
+    _announce("softmax_ex scalar path", rows, cols)
+    x = osm_inputs.softmax_rows(rows, cols, seed=3, sigma=2.0, ninf_prob=0.0)
+    mask = _mask(rows, cols, "bias", 4, torch.float32)
+    lens = torch.tensor([1024, 5, 0, 1023, 700, 2000], dtype=torch.int32)
+    bx = torch.empty(rows * cols + 1, device="cuda")
+    bm = torch.empty(rows * cols + 1, device="cuda")
+    by = torch.empty(rows * cols + 1, device="cuda")
+    bx[1:].copy_(x.flatten().cuda())
+    bm[1:].copy_(mask.flatten().cuda())
+    lc = lens.cuda()
+    st = osm.osm_softmax_rows_ex(bx[1:].data_ptr(), by[1:].data_ptr(), rows, cols, osm.OSM_F32,
+                                 bm[1:].data_ptr(), rows, lc.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == osm.OSM_OK
+    torch.cuda.synchronize()
+    _check_softmax(x, mask, lens, by[1:].view(rows, cols).cpu(), torch.float32)
+
+
+def test_softmax_plain_entry_unchanged_by_null_options():
+    x = osm_inputs.softmax_rows(64, 8192, seed=5).cuda()
+    a = osm.softmax_rows(x)
+    b = torch.empty_like(x)
+    st = osm.osm_softmax_rows_ex(x.data_ptr(), b.data_ptr(), 64, 8192, osm.OSM_F32, 0, 0, 0,
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == osm.OSM_OK
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def _compare_attn(q, k, v, scale, causal, kv_len, bias, o, lse):
+    O, L = attention_ref(q.double().cpu().numpy(), k.double().cpu().numpy(),
+                         v.double().cpu().numpy(), scale, causal,
+                         kv_len=None if kv_len is None else kv_len.cpu().numpy(),
+                         bias=None if bias is None else bias.double().cpu().numpy())
+    og, lg = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    dead = np.isneginf(L)
+    assert (np.isneginf(lg) == dead).all()
+    assert (og[dead] == 0).all()
+    assert np.abs(og - O).max() <= 2e-2
+    assert np.abs(lg[~dead] - L[~dead]).max(initial=0) <= 1e-3
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 100, 256, 301])
+def test_attention_kv_len(N, causal, D):
+    B, H = 4, 2
+    _announce("attn kv_len", B, H, N, D, causal)
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=N + D, device="cuda")
+    kv_len = torch.tensor([N, max(N // 3, 1), 0, N + 7], dtype=torch.int32, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = osm.attn_fwd(q, k, v, scale, causal, kv_len=kv_len)
+    torch.cuda.synchronize()
+    _compare_attn(q, k, v, scale, causal, kv_len, None, o, lse)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,bcast", [(128, "head"), (200, "full"), (77, "head"), (64, "full")])
+def test_attention_bias(N, bcast, causal, D):
+    B, H = 2, 3
+    _announce("attn bias", B, H, N, D, causal, bcast)
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=3 * N + D, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(N)
+    shape = (1, H, N, N) if bcast == "head" else (B, H, N, N)
+    bias = torch.randn(shape, generator=g, device="cuda")
+    bias = torch.where(torch.rand(shape, generator=g, device="cuda") < 0.1, float("-inf"), bias)
+    kv_len = torch.tensor([N, max(N - 50, 1)], dtype=torch.int32, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = osm.attn_fwd(q, k, v, scale, causal, kv_len=kv_len, bias=bias)
+    torch.cuda.synchronize()
+    _compare_attn(q, k, v, scale, causal, kv_len, bias, o, lse)
+
+
+def test_attention_plain_entry_unchanged_by_null_options():
+    q, k, v = osm_inputs.attention_inputs(2, 4, 500, 128, seed=8, device="cuda")
+    a, la = osm.attn_fwd(q, k, v, 0.09, True)
+    o = torch.empty_like(q)
+    lse = torch.empty(2, 4, 500, device="cuda")
+    st = osm.osm_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), 2, 4, 500, 128, 0.09, 1, 0, 0, 0, 0,
+                             torch.cuda.current_stream().cuda_stream)
+    assert st == osm.OSM_OK
+    torch.cuda.synchronize()
+    assert torch.equal(a, o) and torch.equal(la, lse)
