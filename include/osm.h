@@ -98,6 +98,36 @@ int osm_softmax_rows_ex(const void* in, void* out, int64_t rows, int64_t cols, i
                         void* stream);
 
 /*
+ * osm_softmax_rows_split -- row softmax for rows too long for one workgroup.
+ *
+ * The same result as osm_softmax_rows_ex, computed the split-row way of
+ * [Ch6 §6.7.1]: every row is cut into 8192-element chunks, one workgroup per
+ * (row, chunk).  A first kernel reduces each chunk to an online state (m, l)
+ * and stores it in `workspace`; a second merges the row's states with the
+ * combine of [Ch6 §6.4.1] in a fixed order and writes exp(x - M) / L for its
+ * chunk.  The input is read twice and the output written once; use it when
+ * rows * (cols / 8192) is large next to rows alone (a few very long rows).
+ *
+ *   in, out, rows, cols, dtype, mask, mask_rows, row_len
+ *              as osm_softmax_rows_ex (in == out allowed).
+ *   workspace  device memory owned by the caller, 8-byte aligned, at least
+ *              osm_softmax_rows_split_workspace(rows, cols) bytes; its content
+ *              on entry does not matter and is overwritten.  Calls that share
+ *              a workspace must be ordered (same stream).
+ *   workspace_bytes  its size.
+ *
+ * Returns as osm_softmax_rows_ex, plus OSM_ERR_INVALID_ARG for a missing,
+ * misaligned or too small workspace.
+ */
+int osm_softmax_rows_split(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                           const void* mask, int64_t mask_rows, const int32_t* row_len,
+                           void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace osm_softmax_rows_split needs: 8 * rows * ceil(cols / 8192);
+ * -1 for invalid sizes. */
+int64_t osm_softmax_rows_split_workspace(int64_t rows, int64_t cols);
+
+/*
  * osm_attn_fwd -- fused attention forward with per-row log-sum-exp.
  *
  * For every batch b, head h and query row i:
@@ -156,6 +186,40 @@ int osm_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
                     int H, int N, int D, float scale, int causal, const int32_t* kv_len,
                     const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
                     void* stream);
+
+/*
+ * osm_attn_fwd_split -- the fused attention forward with the key range of
+ * every query tile split over several workgroups (split-K).
+ *
+ * The same result as osm_attn_fwd_ex.  Workgroup (b, h, query tile, split)
+ * runs the online softmax over its share of the key tiles and writes its own
+ * normalised partial output O_s (float32) and log-sum-exp LSE_s to
+ * `workspace`; a second kernel merges the splits of every query row with the
+ * combine of [Ch6 §6.4.1] written for normalised partials:
+ *   LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ * Useful when B * H * ceil(N / 128) is small next to the number of compute
+ * units (few heads, long sequences).
+ *
+ *   q .. stride_h   as osm_attn_fwd_ex.
+ *   splits          1 .. 64 workgroups per query tile.
+ *   workspace       device memory owned by the caller, 16-byte aligned, at
+ *                   least osm_attn_fwd_split_workspace(B, H, N, D, splits)
+ *                   bytes; its content on entry does not matter.  Calls that
+ *                   share a workspace must be ordered (same stream).
+ *
+ * Returns as osm_attn_fwd_ex, plus OSM_ERR_INVALID_ARG for splits outside
+ * 1..64 or a missing, misaligned or too small workspace, and
+ * OSM_ERR_UNSUPPORTED when splits > 1 and B * H * N * D / 4 >= 2^32 (the merge
+ * runs one work-item per query row and 4 dimensions).
+ */
+int osm_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int N, int D, float scale, int causal, const int32_t* kv_len,
+                       const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                       int splits, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace osm_attn_fwd_split needs: 4 * splits * B * H * N * (D + 1);
+ * -1 for invalid arguments. */
+int64_t osm_attn_fwd_split_workspace(int B, int H, int N, int D, int splits);
 
 /* Human-readable name of a status code; never NULL, static storage. */
 const char* osm_status_string(int status);

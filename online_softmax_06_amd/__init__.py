@@ -10,16 +10,23 @@ ints; ``stream`` is a hipStream_t handle, 0 for the null stream):
     osm_softmax_rows(in_ptr, out_ptr, rows, cols, dtype, stream) -> status
     osm_softmax_rows_ex(in_ptr, out_ptr, rows, cols, dtype, mask, mask_rows,
                         row_len, stream) -> status
+    osm_softmax_rows_split(in_ptr, out_ptr, rows, cols, dtype, mask, mask_rows,
+                           row_len, workspace, workspace_bytes, stream) -> status
+    osm_softmax_rows_split_workspace(rows, cols) -> bytes
     osm_attn_fwd(q, k, v, o, lse, B, H, N, D, scale, causal, stream) -> status
     osm_attn_fwd_ex(q, k, v, o, lse, B, H, N, D, scale, causal, kv_len, bias,
                     bias_stride_b, bias_stride_h, stream) -> status
+    osm_attn_fwd_split(q, k, v, o, lse, B, H, N, D, scale, causal, kv_len, bias,
+                       bias_stride_b, bias_stride_h, splits, workspace,
+                       workspace_bytes, stream) -> status
+    osm_attn_fwd_split_workspace(B, H, N, D, splits) -> bytes
     osm_status_string(status) -> str
 
 Tensor-level helpers:
 
-    softmax_rows(x, out=None, mask=None, row_len=None) -> Tensor
+    softmax_rows(x, out=None, mask=None, row_len=None, split=False) -> Tensor
     attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None,
-             kv_len=None, bias=None) -> (o, lse)
+             kv_len=None, bias=None, splits=1) -> (o, lse)
 
 If the library has not been built, every call raises ``RuntimeError``; there
 is no fallback implementation.
@@ -32,7 +39,9 @@ import os
 __all__ = [
     "OSM_F32", "OSM_BF16", "OSM_OK", "OSM_ERR_INVALID_ARG", "OSM_ERR_UNSUPPORTED", "OSM_ERR_HIP",
     "OsmError", "lib_path", "load_library", "osm_softmax_rows", "osm_softmax_rows_ex",
-    "osm_attn_fwd", "osm_attn_fwd_ex", "osm_status_string", "osm_version", "softmax_rows",
+    "osm_softmax_rows_split", "osm_softmax_rows_split_workspace",
+    "osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split", "osm_attn_fwd_split_workspace",
+    "osm_status_string", "osm_version", "softmax_rows",
     "attn_fwd",
 ]
 
@@ -71,9 +80,20 @@ def load_library():
     lib.osm_softmax_rows.restype = c_int
     lib.osm_softmax_rows_ex.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_i64, c_vp, c_vp]
     lib.osm_softmax_rows_ex.restype = c_int
+    lib.osm_softmax_rows_split.argtypes = [c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_i64, c_vp,
+                                           c_vp, c_i64, c_vp]
+    lib.osm_softmax_rows_split.restype = c_int
+    lib.osm_softmax_rows_split_workspace.argtypes = [c_i64, c_i64]
+    lib.osm_softmax_rows_split_workspace.restype = c_i64
     lib.osm_attn_fwd_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                     c_f, c_int, c_vp, c_vp, c_i64, c_i64, c_vp]
     lib.osm_attn_fwd_ex.restype = c_int
+    lib.osm_attn_fwd_split.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                       c_f, c_int, c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_i64,
+                                       c_vp]
+    lib.osm_attn_fwd_split.restype = c_int
+    lib.osm_attn_fwd_split_workspace.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    lib.osm_attn_fwd_split_workspace.restype = c_i64
     lib.osm_attn_fwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_f,
                                  c_int, c_vp]
     lib.osm_attn_fwd.restype = c_int
@@ -99,6 +119,17 @@ def osm_softmax_rows_ex(in_ptr, out_ptr, rows, cols, dtype, mask=0, mask_rows=0,
                                               mask_rows, row_len or None, stream)
 
 
+def osm_softmax_rows_split(in_ptr, out_ptr, rows, cols, dtype, mask, mask_rows, row_len,
+                           workspace, workspace_bytes, stream=0):
+    return load_library().osm_softmax_rows_split(in_ptr, out_ptr, rows, cols, dtype,
+                                                 mask or None, mask_rows, row_len or None,
+                                                 workspace or None, workspace_bytes, stream)
+
+
+def osm_softmax_rows_split_workspace(rows, cols):
+    return load_library().osm_softmax_rows_split_workspace(rows, cols)
+
+
 def osm_attn_fwd(q, k, v, o, lse, B, H, N, D, scale, causal, stream=0):
     return load_library().osm_attn_fwd(q, k, v, o, lse, B, H, N, D, scale, int(causal), stream)
 
@@ -108,6 +139,18 @@ def osm_attn_fwd_ex(q, k, v, o, lse, B, H, N, D, scale, causal, kv_len=0, bias=0
     return load_library().osm_attn_fwd_ex(q, k, v, o, lse, B, H, N, D, scale, int(causal),
                                           kv_len or None, bias or None, bias_stride_b,
                                           bias_stride_h, stream)
+
+
+def osm_attn_fwd_split(q, k, v, o, lse, B, H, N, D, scale, causal, kv_len, bias, bias_stride_b,
+                       bias_stride_h, splits, workspace, workspace_bytes, stream=0):
+    return load_library().osm_attn_fwd_split(q, k, v, o, lse, B, H, N, D, scale, int(causal),
+                                             kv_len or None, bias or None, bias_stride_b,
+                                             bias_stride_h, splits, workspace or None,
+                                             workspace_bytes, stream)
+
+
+def osm_attn_fwd_split_workspace(B, H, N, D, splits):
+    return load_library().osm_attn_fwd_split_workspace(B, H, N, D, splits)
 
 
 def osm_status_string(status):
@@ -141,7 +184,7 @@ def _dtype_code(dtype):
     raise TypeError(f"softmax_rows supports float32 and bfloat16, not {dtype}")
 
 
-def softmax_rows(x, out=None, mask=None, row_len=None):
+def softmax_rows(x, out=None, mask=None, row_len=None, split=False):
     """Softmax over the last dimension of a contiguous CUDA tensor.
 
     ``x`` is viewed as [rows, cols] with cols = x.shape[-1].  ``out`` may be
@@ -149,6 +192,8 @@ def softmax_rows(x, out=None, mask=None, row_len=None):
     ``mask`` (same dtype, contiguous, viewed as [mask_rows, cols]; row r uses
     mask row r % mask_rows) is added to the logits; ``row_len`` (int32 CUDA
     tensor of length rows) limits each row, the rest of the row becoming 0.
+    ``split=True`` uses the split-row kernels (a workspace is allocated here,
+    through torch's caching allocator).
     """
     torch = _torch()
     if not x.is_cuda:
@@ -174,6 +219,15 @@ def softmax_rows(x, out=None, mask=None, row_len=None):
                 or not row_len.is_contiguous():
             raise ValueError("row_len must be a contiguous int32 CUDA tensor with one entry per row")
         len_ptr = row_len.data_ptr()
+    if split:
+        need = osm_softmax_rows_split_workspace(rows, cols)
+        ws = torch.empty(max(need, 8), dtype=torch.uint8, device=x.device)
+        st = osm_softmax_rows_split(x.data_ptr(), out.data_ptr(), rows, cols, code, mask_ptr,
+                                    mask_rows, len_ptr, ws.data_ptr(), ws.numel(),
+                                    _stream_handle(x.device))
+        if st != OSM_OK:
+            raise OsmError(st, "osm_softmax_rows_split")
+        return out
     st = osm_softmax_rows_ex(x.data_ptr(), out.data_ptr(), rows, cols, code, mask_ptr, mask_rows,
                              len_ptr, _stream_handle(x.device))
     if st != OSM_OK:
@@ -181,14 +235,17 @@ def softmax_rows(x, out=None, mask=None, row_len=None):
     return out
 
 
-def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None, bias=None):
+def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None, bias=None,
+             splits=1):
     """Fused attention forward on contiguous bfloat16 [B, H, N, D] CUDA tensors.
 
     Returns ``(o, lse)``: o is bfloat16 [B, H, N, D], lse float32 [B, H, N].
     ``scale`` multiplies q.k and defaults to 1/sqrt(D).  ``kv_len`` (int32
     CUDA tensor [B]) hides keys past each batch's length; ``bias`` (float32
     CUDA tensor broadcastable to [B, H, N, N], last two dims contiguous) is
-    added to the scaled scores.
+    added to the scaled scores.  ``splits`` > 1 splits every query tile's key
+    range over that many workgroups (a workspace is allocated here, through
+    torch's caching allocator).
     """
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -220,6 +277,18 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None,
         if bb.stride(3) != 1 or bb.stride(2) != N:
             raise ValueError("bias must have contiguous [N, N] trailing dims")
         bias_ptr, sb, sh = bb.data_ptr(), bb.stride(0), bb.stride(1)
+    if splits > 1:
+        need = osm_attn_fwd_split_workspace(B, H, N, D, splits)
+        if need < 0:
+            raise OsmError(OSM_ERR_INVALID_ARG, "osm_attn_fwd_split_workspace")
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        st = osm_attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, N, D, float(scale), bool(causal), len_ptr,
+                                bias_ptr, sb, sh, splits, ws.data_ptr(), ws.numel(),
+                                _stream_handle(q.device))
+        if st != OSM_OK:
+            raise OsmError(st, "osm_attn_fwd_split")
+        return out, lse
     st = osm_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                          lse.data_ptr(), B, H, N, D, float(scale), bool(causal), len_ptr,
                          bias_ptr, sb, sh, _stream_handle(q.device))

@@ -126,6 +126,17 @@ __device__ __forceinline__ void tile_of(int L, int nqt, int BH, bool causal, int
   qt = causal ? nqt - 1 - rank : rank;
 }
 
+// Split-K variant: each (head, query tile) owns `splits` consecutive ids, so
+// the splits of one query tile are dispatched together.
+__device__ __forceinline__ void tile_of_split(int L, int nqt, int splits, int BH, bool causal,
+                                              int& bh, int& qt, int& split) {
+  int vt;
+  tile_of(L, nqt * splits, BH, false, bh, vt);
+  split = vt % splits;
+  const int rank = vt / splits;
+  qt = causal ? nqt - 1 - rank : rank;
+}
+
 // Per-lane LDS byte offsets inside a K or V buffer, computed once per
 // workgroup.
 // K: lane reads row `col` (and col + 32), 16-byte unit (2c + half) ^ swz(col);
@@ -316,11 +327,16 @@ __device__ __forceinline__ void tile_step(const char* kbuf_next, const char* vbu
   if constexpr (kNext) compute_scores<D>(kbuf_next, off, qreg, snext);
 }
 
-template <int D, bool kCausal, bool kBias>
+// With kSplit, workgroup (head, query tile, split) covers only its share of
+// the key tiles and writes a partial result normalised by its own l -- O_s in
+// float32 and LSE_s -- to o_part / lse_part; attn_split_merge_kernel combines
+// the splits.
+template <int D, bool kCausal, bool kBias, bool kSplit>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int BH,
-    int H, int N, float scale_log2, AttnOptions opt) {
+    int H, int N, float scale_log2, AttnOptions opt, int splits, float* __restrict__ o_part,
+    float* __restrict__ lse_part) {
   using T = Tile<D>;
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
@@ -338,8 +354,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int half = lane >> 5;  // which 8-element half of each 16-wide slice
 
   const int nqt = (N + kBM - 1) / kBM;
-  int bh, qt;
-  tile_of(blockIdx.x, nqt, BH, kCausal, bh, qt);
+  int bh, qt, split = 0;
+  if constexpr (kSplit) {
+    tile_of_split(blockIdx.x, nqt, splits, BH, kCausal, bh, qt, split);
+  } else {
+    tile_of(blockIdx.x, nqt, BH, kCausal, bh, qt);
+  }
   const int64_t head_off = (int64_t)bh * N * D;
   const int head_bytes = N * D * 2;
   const uint16_t* kh = k + head_off;
@@ -355,15 +375,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                             : nullptr;
 
   const int kv_end = kCausal ? min(kvlen, q0 + kBM) : kvlen;
-  const int ntiles = (kv_end + kBN - 1) / kBN;
-  // Last key tile with work for this wave (-1: the wave is past the end).
+  const int ntiles_all = (kv_end + kBN - 1) / kBN;
+  // Key tiles [j_begin, j_end) of this workgroup (all of them without splits).
+  int j_begin = 0, j_end = ntiles_all;
+  if constexpr (kSplit) {
+    const int per = (ntiles_all + splits - 1) / splits;
+    j_begin = min(split * per, ntiles_all);
+    j_end = min(j_begin + per, ntiles_all);
+  }
+  const int ntiles = j_end - j_begin;
+  // Last key tile with work for this wave (below j_begin: none).
   const int jw_last =
-      (qw >= N || ntiles == 0) ? -1 : (kCausal ? min(ntiles - 1, (qw + 31) / kBN) : ntiles - 1);
+      (qw >= N || ntiles == 0) ? -1 : (kCausal ? min(j_end - 1, (qw + 31) / kBN) : j_end - 1);
 
-  // A2 prologue: K_0, V_0 and K_1 in flight.
-  issue_tile<D, T::k_swz>(kbuf0, kh, head_bytes, 0, wave, lane);
-  issue_tile<D, T::v_swz>(vbuf0, vh, head_bytes, 0, wave, lane);
-  if (ntiles > 1) issue_tile<D, T::k_swz>(kbuf1, kh, head_bytes, kBN, wave, lane);
+  // A2 prologue: K and V of the first tile and K of the second in flight.
+  issue_tile<D, T::k_swz>(kbuf0, kh, head_bytes, j_begin * kBN, wave, lane);
+  issue_tile<D, T::v_swz>(vbuf0, vh, head_bytes, j_begin * kBN, wave, lane);
+  if (ntiles > 1) issue_tile<D, T::k_swz>(kbuf1, kh, head_bytes, (j_begin + 1) * kBN, wave, lane);
 
   // A1: this lane's part of Q as the B operand of S^T = K Q^T.
   bf16x8 qreg[kDC];
@@ -383,16 +411,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (jw_last >= 0) compute_scores<D>(kbuf0, off, qreg, sA);
+  if (jw_last >= j_begin) compute_scores<D>(kbuf0, off, qreg, sA);
 
   // A2: at the top of step j, K_{j+1} and V_j have landed and every wave is
   // done with the buffers of K_j and V_{j-1}, which then receive K_{j+2} and
   // V_{j+1}.  One barrier per key tile.
-  for (int j = 0; j < ntiles; j += 2) {
+  for (int j = j_begin; j < j_end; j += 2) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 2 < ntiles) issue_tile<D, T::k_swz>(kbuf0, kh, head_bytes, (j + 2) * kBN, wave, lane);
-    if (j + 1 < ntiles) issue_tile<D, T::v_swz>(vbuf1, vh, head_bytes, (j + 1) * kBN, wave, lane);
+    if (j + 2 < j_end) issue_tile<D, T::k_swz>(kbuf0, kh, head_bytes, (j + 2) * kBN, wave, lane);
+    if (j + 1 < j_end) issue_tile<D, T::v_swz>(vbuf1, vh, head_bytes, (j + 1) * kBN, wave, lane);
     if (j < jw_last) {
       tile_step<D, kCausal, true, kBias>(kbuf1, vbuf0, off, j, N, kvlen, qw, qrow, half,
                                          scale_log2, brow, opt, qreg, sA, sB, oacc, m_run, l_run);
@@ -400,11 +428,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       tile_step<D, kCausal, false, kBias>(kbuf1, vbuf0, off, j, N, kvlen, qw, qrow, half,
                                           scale_log2, brow, opt, qreg, sA, sB, oacc, m_run, l_run);
     }
-    if (j + 1 >= ntiles) break;
+    if (j + 1 >= j_end) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 3 < ntiles) issue_tile<D, T::k_swz>(kbuf1, kh, head_bytes, (j + 3) * kBN, wave, lane);
-    if (j + 2 < ntiles) issue_tile<D, T::v_swz>(vbuf0, vh, head_bytes, (j + 2) * kBN, wave, lane);
+    if (j + 3 < j_end) issue_tile<D, T::k_swz>(kbuf1, kh, head_bytes, (j + 3) * kBN, wave, lane);
+    if (j + 2 < j_end) issue_tile<D, T::v_swz>(vbuf0, vh, head_bytes, (j + 2) * kBN, wave, lane);
     if (j + 1 < jw_last) {
       tile_step<D, kCausal, true, kBias>(kbuf0, vbuf1, off, j + 1, N, kvlen, qw, qrow, half,
                                          scale_log2, brow, opt, qreg, sB, sA, oacc, m_run, l_run);
@@ -417,48 +445,125 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   // A7: O = O / l (deferred division), LSE = ln 2 * (m + log2 l).
   const float l_tot = l_run + swap_halves(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse_val = l_tot > 0.0f ? (finite_ref(m_run) + log2_hw(l_tot)) * kLn2 : kNegInf;
   if (qrow < N) {
-    uint16_t* orow = o + head_off + (int64_t)qrow * D;
+    if constexpr (kSplit) {
+      const int64_t prow = ((int64_t)split * BH + bh) * N + qrow;
+      float* orow = o_part + prow * D;
 #pragma unroll
-    for (int b = 0; b < kDB; ++b) {
+      for (int b = 0; b < kDB; ++b) {
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        // O^T rows b*32 + gq*8 + half*4 + (0..3): four consecutive dims.
-        uint2 w;
-        w.x = pack_bf16x2(oacc[b][gq * 4 + 0] * inv, oacc[b][gq * 4 + 1] * inv);
-        w.y = pack_bf16x2(oacc[b][gq * 4 + 2] * inv, oacc[b][gq * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + b * 32 + gq * 8 + half * 4) = w;
+        for (int gq = 0; gq < 4; ++gq) {
+          const float4 w = make_float4(oacc[b][gq * 4 + 0] * inv, oacc[b][gq * 4 + 1] * inv,
+                                       oacc[b][gq * 4 + 2] * inv, oacc[b][gq * 4 + 3] * inv);
+          *reinterpret_cast<float4*>(orow + b * 32 + gq * 8 + half * 4) = w;
+        }
       }
-    }
-    if (half == 0) {
-      lse[(int64_t)bh * N + qrow] =
-          l_tot > 0.0f ? (finite_ref(m_run) + log2_hw(l_tot)) * kLn2 : kNegInf;
+      if (half == 0) lse_part[prow] = lse_val;
+    } else {
+      uint16_t* orow = o + head_off + (int64_t)qrow * D;
+#pragma unroll
+      for (int b = 0; b < kDB; ++b) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          // O^T rows b*32 + gq*8 + half*4 + (0..3): four consecutive dims.
+          uint2 w;
+          w.x = pack_bf16x2(oacc[b][gq * 4 + 0] * inv, oacc[b][gq * 4 + 1] * inv);
+          w.y = pack_bf16x2(oacc[b][gq * 4 + 2] * inv, oacc[b][gq * 4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + b * 32 + gq * 8 + half * 4) = w;
+        }
+      }
+      if (half == 0) lse[(int64_t)bh * N + qrow] = lse_val;
     }
   }
 }
 
-template <int D, bool kCausal, bool kBias>
+// Merge the splits of every query row: with M = max_s LSE_s and
+// w_s = e^(LSE_s - M), LSE = M + log sum_s w_s and O = sum_s w_s O_s / sum_s w_s
+// -- the (m, l) combine of §6.4.1 written for normalised partial outputs.
+// One thread per (row, 4 dims); splits are folded in index order.
+template <int D>
+__global__ __launch_bounds__(256) void attn_split_merge_kernel(const float* __restrict__ o_part,
+                                                                const float* __restrict__ lse_part,
+                                                                uint16_t* __restrict__ o,
+                                                                float* __restrict__ lse,
+                                                                int64_t rows, int splits) {
+  constexpr int kQuads = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * kQuads) return;
+  const int64_t row = idx / kQuads;
+  const int dq = (int)(idx % kQuads);
+  float M = kNegInf;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, lse_part[s * rows + row]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.0f;
+  if (M != kNegInf) {
+    for (int s = 0; s < splits; ++s) {
+      const float w = exp2_hw((lse_part[s * rows + row] - M) * kLog2e);
+      const float4 p = *reinterpret_cast<const float4*>(o_part + (s * rows + row) * D + dq * 4);
+      acc.x += w * p.x;
+      acc.y += w * p.y;
+      acc.z += w * p.z;
+      acc.w += w * p.w;
+      L += w;
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  uint2 out;
+  out.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+  out.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2*>(o + row * D + dq * 4) = out;
+  if (dq == 0) lse[row] = L > 0.0f ? M + log2_hw(L) * kLn2 : kNegInf;
+}
+
+template <int D, bool kCausal, bool kBias, bool kSplit>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int H,
-                  int N, float scale, const AttnOptions& opt, hipStream_t s) {
+                  int N, float scale, const AttnOptions& opt, int splits, float* o_part,
+                  float* lse_part, hipStream_t s) {
   const int nqt = (N + kBM - 1) / kBM;
   const float scale_log2 = scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, kCausal, kBias>), dim3(nqt * BH), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, kCausal, kBias, kSplit>),
+                     dim3(nqt * BH * (kSplit ? splits : 1)), dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, H, N,
-                     scale_log2, opt);
+                     scale_log2, opt, splits, o_part, lse_part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !kSplit) return e;
+  const int64_t rows = (int64_t)BH * N;
+  const int64_t threads = rows * (D / 4);
+  hipLaunchKernelGGL((attn_split_merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, s, o_part, lse_part, static_cast<uint16_t*>(o), lse, rows,
+                     splits);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool kSplit>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                    int H, int N, float scale, bool causal, const AttnOptions& opt,
-                    hipStream_t s) {
+                    int H, int N, float scale, bool causal, const AttnOptions& opt, int splits,
+                    float* o_part, float* lse_part, hipStream_t s) {
   if (opt.bias != nullptr) {
-    return causal ? launch<D, true, true>(q, k, v, o, lse, BH, H, N, scale, opt, s)
-                  : launch<D, false, true>(q, k, v, o, lse, BH, H, N, scale, opt, s);
+    return causal ? launch<D, true, true, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
+                                                  o_part, lse_part, s)
+                  : launch<D, false, true, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
+                                                   o_part, lse_part, s);
   }
-  return causal ? launch<D, true, false>(q, k, v, o, lse, BH, H, N, scale, opt, s)
-                : launch<D, false, false>(q, k, v, o, lse, BH, H, N, scale, opt, s);
+  return causal ? launch<D, true, false, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
+                                                 o_part, lse_part, s)
+                : launch<D, false, false, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
+                                                  o_part, lse_part, s);
+}
+
+AttnOptions make_options(int N, float scale, const int32_t* kv_len, const float* bias,
+                         int64_t bias_stride_b, int64_t bias_stride_h) {
+  AttnOptions opt;
+  opt.kv_len = kv_len;
+  opt.bias = bias;
+  opt.bias_stride_b = bias_stride_b;
+  opt.bias_stride_h = bias_stride_h;
+  opt.inv_scale = 1.0f / scale;
+  opt.bias_vec = bias != nullptr && (N % 4) == 0 && (bias_stride_b % 4) == 0 &&
+                 (bias_stride_h % 4) == 0 && (reinterpret_cast<uintptr_t>(bias) % 16) == 0;
+  return opt;
 }
 
 }  // namespace
@@ -468,16 +573,32 @@ hipError_t attn_fwd_launch(const void* q, const void* k, const void* v, void* o,
                            const int32_t* kv_len, const float* bias, int64_t bias_stride_b,
                            int64_t bias_stride_h, hipStream_t stream) {
   const int BH = B * H;
-  AttnOptions opt;
-  opt.kv_len = kv_len;
-  opt.bias = bias;
-  opt.bias_stride_b = bias_stride_b;
-  opt.bias_stride_h = bias_stride_h;
-  opt.inv_scale = 1.0f / scale;
-  opt.bias_vec = bias != nullptr && (N % 4) == 0 && (bias_stride_b % 4) == 0 &&
-                 (bias_stride_h % 4) == 0 && (reinterpret_cast<uintptr_t>(bias) % 16) == 0;
-  if (D == 64) return launch_d<64>(q, k, v, o, lse, BH, H, N, scale, causal, opt, stream);
-  return launch_d<128>(q, k, v, o, lse, BH, H, N, scale, causal, opt, stream);
+  const AttnOptions opt = make_options(N, scale, kv_len, bias, bias_stride_b, bias_stride_h);
+  if (D == 64)
+    return launch_d<64, false>(q, k, v, o, lse, BH, H, N, scale, causal, opt, 1, nullptr, nullptr,
+                               stream);
+  return launch_d<128, false>(q, k, v, o, lse, BH, H, N, scale, causal, opt, 1, nullptr, nullptr,
+                              stream);
+}
+
+int64_t attn_split_workspace(int B, int H, int N, int D, int splits) {
+  return (int64_t)splits * B * H * N * (D + 1) * (int64_t)sizeof(float);
+}
+
+hipError_t attn_fwd_split_launch(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int H, int N, int D, float scale, bool causal,
+                                 const int32_t* kv_len, const float* bias, int64_t bias_stride_b,
+                                 int64_t bias_stride_h, int splits, void* workspace,
+                                 hipStream_t stream) {
+  const int BH = B * H;
+  const AttnOptions opt = make_options(N, scale, kv_len, bias, bias_stride_b, bias_stride_h);
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = o_part + (int64_t)splits * BH * N * D;
+  if (D == 64)
+    return launch_d<64, true>(q, k, v, o, lse, BH, H, N, scale, causal, opt, splits, o_part,
+                              lse_part, stream);
+  return launch_d<128, true>(q, k, v, o, lse, BH, H, N, scale, causal, opt, splits, o_part,
+                             lse_part, stream);
 }
 
 }  // namespace osm

@@ -15,6 +15,14 @@ hipError_t softmax_rows_launch(const void* in, void* out, int64_t rows, int cols
                                bool vector_path, const void* mask, int64_t mask_rows,
                                const int32_t* row_len, hipStream_t stream);
 
+// Split-row softmax: bytes of workspace needed, and the two-stage launch
+// (workspace holds one float2 state per (row, 8192-element chunk)).
+int64_t softmax_split_workspace(int64_t rows, int64_t cols);
+hipError_t softmax_rows_split_launch(const void* in, void* out, int64_t rows, int cols, int dtype,
+                                     bool vector_path, const void* mask, int64_t mask_rows,
+                                     const int32_t* row_len, void* workspace,
+                                     hipStream_t stream);
+
 // Fused attention forward, bfloat16 [B, H, N, D] in/out, float32 LSE [B, H, N].
 // D must be 64 or 128.  kv_len (nullable, int32 [B]) limits the keys of each
 // batch; bias (nullable, fp32) is added to the scaled scores, element
@@ -23,5 +31,14 @@ hipError_t attn_fwd_launch(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int N, int D, float scale, bool causal,
                            const int32_t* kv_len, const float* bias, int64_t bias_stride_b,
                            int64_t bias_stride_h, hipStream_t stream);
+
+// Split-K attention: workspace bytes (partial O in float32 plus partial LSE
+// for every split), and the launch of the partial and merge kernels.
+int64_t attn_split_workspace(int B, int H, int N, int D, int splits);
+hipError_t attn_fwd_split_launch(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int H, int N, int D, float scale, bool causal,
+                                 const int32_t* kv_len, const float* bias, int64_t bias_stride_b,
+                                 int64_t bias_stride_h, int splits, void* workspace,
+                                 hipStream_t stream);
 
 }  // namespace osm

@@ -341,6 +341,126 @@ hipError_t dispatch(const void* in, void* out, int64_t rows, int cols, const Row
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Split rows ("Ch.6" §6.7.1: a row too long for one block is shared by several
+// blocks, with a second stage to merge).  Each workgroup owns one chunk of
+// kSplitChunk elements of one row.
+//   stage 1: load the chunk, reduce it to one online state (m, l) -- the same
+//            lane state, wavefront butterfly and LDS merge as above -- and
+//            store it in the workspace at [row][chunk];
+//   stage 2: merge the row's chunk states (lane i folds states i, i + 256, ...,
+//            then the same butterfly and LDS merge, in a fixed order), reload
+//            the chunk and write exp(x - M) / L.
+// Traffic: 2 reads + 1 write per element, spread over rows x chunks workgroups.
+// ---------------------------------------------------------------------------
+constexpr int kSplitThreads = 256;
+constexpr int kSplitChunk = 8192;  // elements per workgroup
+
+template <typename E, int VEC>
+__device__ __forceinline__ void load_chunk(const void* in, int64_t base, int64_t mbase, int c0,
+                                           int cols, int len, const RowOptions& opt, int t,
+                                           float (&x)[kSplitChunk / kSplitThreads]) {
+  constexpr int NV = kSplitChunk / kSplitThreads / VEC;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int e0 = c0 + (k * kSplitThreads + t) * VEC;  // first element of the vector
+    if (e0 < cols) {
+      load_masked<E, VEC>(in, base, mbase, e0 / VEC, len, opt, &x[k * VEC]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) x[k * VEC + j] = kNegInf;
+    }
+  }
+}
+
+template <typename E, int VEC>
+__global__ __launch_bounds__(kSplitThreads) void softmax_split_stats_kernel(
+    const void* in, int64_t rows, int cols, int chunks, RowOptions opt, float2* state) {
+  constexpr int kN = kSplitChunk / kSplitThreads;
+  __shared__ float2 slots[2][kSplitThreads / 64];
+  const int t = threadIdx.x;
+  int parity = 0;
+  for (int64_t w = blockIdx.x; w < rows * chunks; w += gridDim.x, parity ^= 1) {
+    const int64_t row = w / chunks;
+    const int c0 = (int)(w % chunks) * kSplitChunk;
+    const int len = opt.length(row, cols);
+    const int64_t mbase = opt.mask ? (row % opt.mask_rows) * (int64_t)cols : 0;
+    float x[kN];
+    load_chunk<E, VEC>(in, row * (int64_t)cols, mbase, c0, cols, len, opt, t, x);
+    float m = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kN; ++i) m = fmaxf(m, x[i]);
+    const float ref = finite_ref(m);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) x[i] = exp2_hw((x[i] - ref) * kLog2e);
+    float l = tree_sum<kN>(x);
+    wave_combine_state(m, l);
+    lds_combine<kSplitThreads / 64>(m, l, slots[parity], t / 64);
+    if (t == 0) state[w] = make_float2(m, l);
+  }
+}
+
+template <typename E, int VEC>
+__global__ __launch_bounds__(kSplitThreads) void softmax_split_norm_kernel(
+    const void* in, void* out, int64_t rows, int cols, int chunks, RowOptions opt,
+    const float2* state) {
+  constexpr int kN = kSplitChunk / kSplitThreads;
+  constexpr int NV = kN / VEC;
+  __shared__ float2 slots[2][kSplitThreads / 64];
+  const int t = threadIdx.x;
+  int parity = 0;
+  for (int64_t w = blockIdx.x; w < rows * chunks; w += gridDim.x, parity ^= 1) {
+    const int64_t row = w / chunks;
+    const int c0 = (int)(w % chunks) * kSplitChunk;
+    // Merge the row's chunk states.
+    float m = kNegInf, l = 0.0f;
+    for (int c = t; c < chunks; c += kSplitThreads) {
+      const float2 st = state[row * chunks + c];
+      combine_state(m, l, st.x, st.y);
+    }
+    wave_combine_state(m, l);
+    lds_combine<kSplitThreads / 64>(m, l, slots[parity], t / 64);
+    const float r = finite_ref(m);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    // Normalise this chunk.
+    const int len = opt.length(row, cols);
+    const int64_t base = row * (int64_t)cols;
+    const int64_t mbase = opt.mask ? (row % opt.mask_rows) * (int64_t)cols : 0;
+    float x[kN];
+    load_chunk<E, VEC>(in, base, mbase, c0, cols, len, opt, t, x);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int e0 = c0 + (k * kSplitThreads + t) * VEC;
+      if (e0 < cols) {
+        float y[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) y[j] = exp2_hw((x[k * VEC + j] - r) * kLog2e) * inv;
+        if constexpr (VEC == 1) {
+          E::store1(out, base + e0, y[0]);
+        } else {
+          __builtin_nontemporal_store(
+              E::pack(y),
+              reinterpret_cast<u32x4*>(static_cast<char*>(out) + (base + e0) * (16 / VEC)));
+        }
+      }
+    }
+  }
+}
+
+template <typename E, int VEC>
+hipError_t launch_split(const void* in, void* out, int64_t rows, int cols, const RowOptions& opt,
+                        float2* state, hipStream_t s) {
+  const int chunks = (cols + kSplitChunk - 1) / kSplitChunk;
+  const unsigned grid = grid_for(rows * chunks);
+  hipLaunchKernelGGL((softmax_split_stats_kernel<E, VEC>), dim3(grid), dim3(kSplitThreads), 0, s,
+                     in, rows, cols, chunks, opt, state);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((softmax_split_norm_kernel<E, VEC>), dim3(grid), dim3(kSplitThreads), 0, s,
+                     in, out, rows, cols, chunks, opt, state);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t softmax_rows_launch(const void* in, void* out, int64_t rows, int cols, int dtype,
@@ -353,6 +473,28 @@ hipError_t softmax_rows_launch(const void* in, void* out, int64_t rows, int cols
   }
   return vector_path ? dispatch<Elem<Bf16>, 8>(in, out, rows, cols, opt, s)
                      : dispatch<Elem<Bf16>, 1>(in, out, rows, cols, opt, s);
+}
+
+}  // namespace osm
+
+namespace osm {
+
+int64_t softmax_split_workspace(int64_t rows, int64_t cols) {
+  const int64_t chunks = (cols + kSplitChunk - 1) / kSplitChunk;
+  return rows * chunks * (int64_t)sizeof(float2);
+}
+
+hipError_t softmax_rows_split_launch(const void* in, void* out, int64_t rows, int cols, int dtype,
+                                     bool vector_path, const void* mask, int64_t mask_rows,
+                                     const int32_t* row_len, void* workspace, hipStream_t s) {
+  const RowOptions opt{mask, mask_rows > 0 ? mask_rows : 1, row_len};
+  float2* state = static_cast<float2*>(workspace);
+  if (dtype == 0) {
+    return vector_path ? launch_split<Elem<float>, 4>(in, out, rows, cols, opt, state, s)
+                       : launch_split<Elem<float>, 1>(in, out, rows, cols, opt, state, s);
+  }
+  return vector_path ? launch_split<Elem<Bf16>, 8>(in, out, rows, cols, opt, state, s)
+                     : launch_split<Elem<Bf16>, 1>(in, out, rows, cols, opt, state, s);
 }
 
 }  // namespace osm

@@ -31,8 +31,11 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["osm_attn_fwd", "osm_attn_fwd_ex", "osm_softmax_rows",
-                                     "osm_softmax_rows_ex", "osm_status_string", "osm_version"]
+    assert _declared_functions() == ["osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split",
+                                     "osm_attn_fwd_split_workspace", "osm_softmax_rows",
+                                     "osm_softmax_rows_ex", "osm_softmax_rows_split",
+                                     "osm_softmax_rows_split_workspace", "osm_status_string",
+                                     "osm_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -132,3 +135,40 @@ def test_attention_ex_argument_checks(lib, kw, expect):
              causal=0, kv_len=0, bias=0, bias_stride_b=0, bias_stride_h=0)
     a.update(kw)
     assert osm.osm_attn_fwd_ex(*a.values(), 0) == expect
+
+
+def test_split_workspace_size(lib):
+    assert osm.osm_softmax_rows_split_workspace(4, 8192) == 4 * 8
+    assert osm.osm_softmax_rows_split_workspace(3, 8193) == 3 * 2 * 8
+    assert osm.osm_softmax_rows_split_workspace(2, 1 << 20) == 2 * 128 * 8
+    assert osm.osm_softmax_rows_split_workspace(0, 5) == 0
+    assert osm.osm_softmax_rows_split_workspace(-1, 5) == -1
+    assert osm.osm_softmax_rows_split_workspace(5, 2 ** 31) == -1
+
+
+@pytest.mark.parametrize("ws,wsb,expect", [
+    (0, 1 << 20, osm.OSM_ERR_INVALID_ARG),         # no workspace
+    (FAKE, 8, osm.OSM_ERR_INVALID_ARG),            # too small (needs 2 * 4 * 8)
+    (FAKE + 4, 1 << 20, osm.OSM_ERR_INVALID_ARG),  # misaligned
+])
+def test_split_argument_checks(lib, ws, wsb, expect):
+    assert osm.osm_softmax_rows_split(FAKE, FAKE, 2, 30000, 0, 0, 0, 0, ws, wsb, 0) == expect
+
+
+def test_attn_split_workspace_size(lib):
+    assert osm.osm_attn_fwd_split_workspace(1, 2, 100, 64, 3) == 4 * 3 * 2 * 100 * 65
+    assert osm.osm_attn_fwd_split_workspace(1, 1, 10, 96, 2) == -1
+    assert osm.osm_attn_fwd_split_workspace(1, 1, 10, 64, 0) == -1
+    assert osm.osm_attn_fwd_split_workspace(1, 1, 10, 64, 65) == -1
+
+
+@pytest.mark.parametrize("splits,ws,wsb,expect", [
+    (0, FAKE, 1 << 30, osm.OSM_ERR_INVALID_ARG),
+    (65, FAKE, 1 << 30, osm.OSM_ERR_INVALID_ARG),
+    (2, 0, 1 << 30, osm.OSM_ERR_INVALID_ARG),
+    (2, FAKE, 16, osm.OSM_ERR_INVALID_ARG),
+    (2, FAKE + 8, 1 << 30, osm.OSM_ERR_INVALID_ARG),
+])
+def test_attn_split_argument_checks(lib, splits, ws, wsb, expect):
+    assert osm.osm_attn_fwd_split(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 300, 128, 0.1, 1, 0, 0, 0, 0,
+                                  splits, ws, wsb, 0) == expect
