@@ -85,29 +85,35 @@ struct Tile {
   }
 };
 
-// Issue the global->LDS copy of one K or V tile (keys [k0, k0 + 64)) into
-// `buf`.  Instruction i of wave w fills LDS units [(w * kLoadsPerWave + i) *
-// 64, +64) of the tile, one 16-byte unit per lane; `swz` is the tile's row
-// swizzle.  Keys at or past the end of the head read as zeros.
-template <int D, int (*Swz)(int)>
-__device__ __forceinline__ void issue_tile(char* buf, const uint16_t* base, int head_bytes, int k0,
-                                           int wave, int lane) {
-  // The buffer-to-LDS builtins exist only for the device; the host pass of
-  // this single-source file sees an empty body.
-#if defined(__HIP_DEVICE_COMPILE__)
-  using T = Tile<D>;
-  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, head_bytes, kBufferFlags);
-#pragma unroll
-  for (int i = 0; i < T::kLoadsPerWave; ++i) {
-    const int inst = wave * T::kLoadsPerWave + i;
-    const int p = inst * 64 + lane;                 // physical unit in the tile
-    const int row = p / T::kUnits, pu = p % T::kUnits;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, OSM_LDS(buf + inst * 1024), 16,
-                                             (k0 + row) * (D * 2) + ((pu ^ Swz(row)) << 4), 0, 0,
-                                             0);
+// Global->LDS copy of kRows key rows [k0, k0 + kRows) of K or V into `buf`
+// (row-major, 16-byte units XOR-swizzled by `Swz`), one instruction at a
+// time: instruction i of wave w fills LDS units [(w * kPerWave + i) * 64,
+// +64), one 16-byte unit per lane.  The key offset goes in the scalar offset,
+// the lane's part in a loop-invariant vector offset.  Keys at or past the end
+// of the head (the descriptor's range) read as zeros; k0 = N therefore turns
+// an instruction into a harmless zero fill without memory traffic.
+template <int D, int kRows>
+struct RowCopy {
+  static constexpr int kUnits = D / 8;
+  static constexpr int kPerWave = kRows * kUnits / 64 / kWaves;
+  static_assert(kPerWave >= 1, "every wave issues at least one load");
+  template <int (*Swz)(int)>
+  __device__ static int lane_offset(int wave, int lane, int i) {
+    const int p = (wave * kPerWave + i) * 64 + lane;  // physical unit in the block
+    const int row = p / kUnits, pu = p % kUnits;
+    return row * (D * 2) + ((pu ^ Swz(row)) << 4);
   }
+  __device__ static void issue(char* buf, const uint16_t* base, int head_bytes, int k0, int wave,
+                               int i, int voff) {
+    // The buffer-to-LDS builtins exist only for the device; the host pass of
+    // this single-source file sees an empty body.
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, head_bytes, kBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, OSM_LDS(buf + (wave * kPerWave + i) * 1024), 16,
+                                             voff, k0 * (D * 2), 0, 0);
 #endif
-}
+  }
+};
 
 // Map a linear workgroup id to (batch*head, query tile).  Workgroups are
 // dispatched round-robin over the 8 XCDs; when B*H is a multiple of 8 all
@@ -137,11 +143,10 @@ __device__ __forceinline__ void tile_of_split(int L, int nqt, int splits, int BH
   qt = causal ? nqt - 1 - rank : rank;
 }
 
-// Per-lane LDS byte offsets inside a K or V buffer, computed once per
-// workgroup.
-// K: lane reads row `col` (and col + 32), 16-byte unit (2c + half) ^ swz(col);
-// since the swizzle keeps bit 0 of the unit apart from c's bits, the offset
-// for slice c is k ^ (c << 5), and rows col + 32 sit 32 rows further.
+// Per-lane LDS byte offsets, computed once per workgroup.
+// K: lane reads row `col` of a 32-row slot, 16-byte unit (2c + half) ^
+// swz(col); since the swizzle keeps bit 0 of the unit apart from c's bits,
+// the offset for slice c is k ^ (c << 5).
 // V: lane reads key row `vkey` (+ 16 kc + 8 part) at dims b*32 + vd; the
 // swizzle depends on row & 7 only, so the other rows are constant offsets.
 template <int D>
@@ -171,37 +176,24 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
 }
 
-// A3: S^T = K Q^T for one key tile (16 products at D = 128) from `kbuf`.
-// K operands are read two slices ahead of the products that use them.
+// A3 for one 32-key sub-tile: S^T (32 keys x 32 queries) = K Q^T from the
+// 32-row K slot `kslot` (kDC products; K operands read two slices ahead).
 template <int D>
-__device__ __forceinline__ void compute_scores(const char* kbuf, const LaneOffsets<D>& off,
-                                               const bf16x8 (&qreg)[D / 16], f32x16 (&s)[2]) {
+__device__ __forceinline__ f32x16 sub_scores(const char* kslot, const LaneOffsets<D>& off,
+                                             const bf16x8 (&qreg)[D / 16]) {
   constexpr int kDC = D / 16;
-  constexpr int kRow = D * 2;
-  s[0] = f32x16{};
-  s[1] = f32x16{};
-  bf16x8 ka[3][2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const char* pk = kbuf + (off.k ^ (c << 5));
-    ka[c][0] = *reinterpret_cast<const bf16x8*>(pk);
-    ka[c][1] = *reinterpret_cast<const bf16x8*>(pk + 32 * kRow);
-  }
+  f32x16 s = f32x16{};
+  bf16x8 ka[3];
+  ka[0] = *reinterpret_cast<const bf16x8*>(kslot + off.k);
+  ka[1] = *reinterpret_cast<const bf16x8*>(kslot + (off.k ^ (1 << 5)));
 #pragma unroll
   for (int c = 0; c < kDC; ++c) {
-    if (c + 2 < kDC) {
-      const char* pk = kbuf + (off.k ^ ((c + 2) << 5));
-      ka[(c + 2) % 3][0] = *reinterpret_cast<const bf16x8*>(pk);
-      ka[(c + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(pk + 32 * kRow);
-    }
-    s[0] = mfma32(ka[c % 3][0], qreg[c], s[0]);
-    s[1] = mfma32(ka[c % 3][1], qreg[c], s[1]);
+    if (c + 2 < kDC) ka[(c + 2) % 3] = *reinterpret_cast<const bf16x8*>(kslot + (off.k ^ ((c + 2) << 5)));
+    s = mfma32(ka[c % 3], qreg[c], s);
   }
+  return s;
 }
 
-// One key tile j for one wavefront: mask and softmax the scores S_j held in
-// `scur`, then O^T += V_j^T P_j^T; with kNext, then form the scores of tile
-// j + 1 into `snext`, so 32 matrix products run back to back per tile.
 // Optional fused inputs: per-batch key lengths (keys at or past kv_len are
 // hidden) and an additive fp32 bias on the scaled scores, element (b, h, i, j)
 // at bias[b * stride_b + h * stride_h + i * N + j].
@@ -213,267 +205,505 @@ struct AttnOptions {
   bool bias_vec;    // N, strides and base allow 16-byte bias loads
 };
 
-// Add the bias of this lane's query row to its 32 raw scores of tile k0.
-__device__ __forceinline__ void add_bias(f32x16 (&s)[2], const float* brow, int k0, int half,
-                                         int N, const AttnOptions& opt) {
+// Add the bias of this lane's query row to its 16 raw scores of the sub-tile
+// starting at key k0.  Score i is key k0 + (i / 4) * 8 + half * 4 + i % 4.
+__device__ __forceinline__ void add_bias(f32x16& s, const float* brow, int k0, int half, int N,
+                                         const AttnOptions& opt) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int key = k0 + kb * 32 + g * 8 + half * 4;  // 4 consecutive keys
-      float b4[4];
-      if (opt.bias_vec) {
-        if (key < N) {
-          const float4 f = *reinterpret_cast<const float4*>(brow + key);
-          b4[0] = f.x; b4[1] = f.y; b4[2] = f.z; b4[3] = f.w;
-        } else {
-          b4[0] = b4[1] = b4[2] = b4[3] = 0.0f;
-        }
+  for (int g = 0; g < 4; ++g) {
+    const int key = k0 + g * 8 + half * 4;  // 4 consecutive keys
+    float b4[4];
+    if (opt.bias_vec) {
+      if (key < N) {
+        const float4 f = *reinterpret_cast<const float4*>(brow + key);
+        b4[0] = f.x; b4[1] = f.y; b4[2] = f.z; b4[3] = f.w;
       } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b4[t] = key + t < N ? brow[key + t] : 0.0f;
+        b4[0] = b4[1] = b4[2] = b4[3] = 0.0f;
       }
+    } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s[kb][g * 4 + t] += b4[t] * opt.inv_scale;
+      for (int t = 0; t < 4; ++t) b4[t] = key + t < N ? brow[key + t] : 0.0f;
     }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s[g * 4 + t] += b4[t] * opt.inv_scale;
   }
 }
 
-template <int D, bool kCausal, bool kNext, bool kBias>
-__device__ __forceinline__ void tile_step(const char* kbuf_next, const char* vbuf,
-                                          const LaneOffsets<D>& off, int j, int N, int kvlen,
-                                          int qw, int qrow, int half, float scale_log2,
-                                          const float* brow, const AttnOptions& opt,
-                                          const bf16x8 (&qreg)[D / 16], f32x16 (&scur)[2],
-                                          f32x16 (&snext)[2], f32x16 (&oacc)[D / 32],
-                                          float& m_run, float& l_run) {
-  constexpr int kDC = D / 16;
-  constexpr int kDB = D / 32;
-  constexpr int kRow = D * 2;  // bytes per key row
-  const int k0 = j * kBN;
+// Per-wavefront state of the key loop.
+template <int D>
+struct WaveState {
+  bf16x8 qreg[D / 16];   // this lane's part of Q: B operand of S^T = K Q^T
+  f32x16 oacc[D / 32];   // O^T accumulators (32 dims x 32 queries each)
+  f32x16 sc;             // scores of the current 32-key sub-tile
+  float m_run;           // exponent reference, in units of log2(e) * scale * S
+  float l_run;           // this lane's half of the running sum
+};
+
+// One 32-key sub-tile s (keys [32 s, 32 s + 32), the half kKb of its 64-key
+// tile) for one wavefront, in two phases.
+//   Phase 1: the scores of sub-tile s + 1 (with kNext) are formed on the
+//            matrix core from `kslot_next` while the vector unit masks the
+//            current scores, finds their row max and exponentiates them;
+//            neither depends on the other, so both units work side by side.
+//   Phase 2: O is rescaled by alpha (only when some lane needs it), then
+//            O^T += V^T P^T on the two 16-key slices of this sub-tile, fed by
+//            transposed V reads from `vtile`, while the vector unit packs P to
+//            bfloat16 and sums it.
+// Each phase is a sequence of short regions (one or two products, the LDS
+// reads they need two regions later, a share of the vector work) fenced by
+// sched_barrier, so the compiler keeps this interleaving.  `copy(i)` issues
+// this wave's i-th global->LDS copy instruction of the sub-step (if any).
+template <int D, bool kCausal, int kKb, bool kNext, bool kMask, bool kBias, typename Copy>
+__device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_next,
+                                         const char* vtile, const LaneOffsets<D>& off, int s,
+                                         int N, int kvlen, int qrow, int half, float scale_log2,
+                                         const float* brow, const AttnOptions& opt,
+                                         const Copy& copy) {
+  constexpr int kDC = D / 16;   // 16-wide slices of the head dimension
+  constexpr int kDB = D / 32;   // 32-dim blocks of O^T
+  constexpr int kPV = 2 * kDB;  // products of phase 2
+  constexpr int kRow = D * 2;   // bytes per key row
+  const int k0 = s * 32;
+  f32x16& sc = st.sc;
 
   if constexpr (kBias) {
-    if (qrow < N) add_bias(scur, brow, k0, half, N, opt);
-  }
-  // A4: hide keys past the causal diagonal or past the valid keys.
-  const bool need_mask = (kCausal && k0 + kBN - 1 > qw) || (k0 + kBN > kvlen);
-  if (need_mask) {
-    // Keys k0 + (i / 4) * 8 + half * 4 + i % 4 (+ 32) are visible when below
-    // lim; compare the constant part against lim - k0 - 4 * half.
-    const int lim = (kCausal ? min(kvlen, qrow + 1) : kvlen) - k0 - half * 4;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = (i >> 2) * 8 + (i & 3);
-      scur[0][i] = kk < lim ? scur[0][i] : kNegInf;
-      scur[1][i] = kk + 32 < lim ? scur[1][i] : kNegInf;
-    }
+    if (qrow < N) add_bias(sc, brow, k0, half, N, opt);
   }
 
-  // A5: online-softmax update for this lane's query row.
-  float mx = __builtin_fmaxf(scur[0][0], scur[1][0]);
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mx = max3(mx, scur[0][i], scur[1][i]);
-  mx = __builtin_fmaxf(mx, swap_halves(mx));
-  const float mt = mx * scale_log2;
-  const float m_new = mt > m_run + kLag ? mt : m_run;
-  const float ref = finite_ref(m_new);
-  const float alpha = exp2_hw(m_run - ref);
-  float psum = 0.0f;
-  bf16x8 pb[4];
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
-    uint32_t w[4];
-#pragma unroll
-    for (int jj = 0; jj < 8; jj += 2) {
-      const float sa = scur[kc >> 1][(kc & 1) * 8 + jj];
-      const float sb = scur[kc >> 1][(kc & 1) * 8 + jj + 1];
-      const float pa = exp2_hw(__builtin_fmaf(sa, scale_log2, -ref));
-      const float pbv = exp2_hw(__builtin_fmaf(sb, scale_log2, -ref));
-      psum += pa + pbv;
-      w[jj / 2] = pack_bf16x2(pa, pbv);
-    }
-    pb[kc] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  // Phase 1.
+  bf16x8 ka[3];
+  auto read_k = [&](int c) {
+    ka[c % 3] = *reinterpret_cast<const bf16x8*>(kslot_next + (off.k ^ (c << 5)));
+  };
+  // V operands of phase 2, two products ahead; product i is (kc2, b) =
+  // (i / kDB, i % kDB), key slice kc = 2 kKb + kc2 of the 64-key tile.
+  bf16x8 va[3];
+  auto read_v = [&](int i) {
+    const int kc = 2 * kKb + i / kDB, b = i % kDB;
+    const char* p0 = vtile + off.v[b] + kc * 16 * kRow;
+    // Transposed V reads: lane (group g = lane / 16, r = lane % 16) supplies
+    // the address of dims [d0 + 4 (r % 4), +4) of key row base + r / 4; it
+    // receives dims d0 + r of keys base .. base + 3 (d0 = 32 b + 16 (g % 2)).
+    const s16x4 v0 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p0 + 8 * kRow));
+    va[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  f32x16 sn = f32x16{};
+  if constexpr (kNext) {
+    read_k(0);
+    read_k(1);
   }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
+  float p[16];
+  float m_new = 0.0f, ref = 0.0f, alpha = 1.0f;
+  constexpr int kExpRegions = kDC - 1;
+#pragma unroll
+  for (int c = 0; c < kDC; ++c) {
+    if constexpr (kNext) {
+      if (c + 2 < kDC) read_k(c + 2);
+      sn = mfma32(ka[c % 3], st.qreg[c], sn);
+    }
+    // One global->LDS copy instruction per region (regions 1..): spread out,
+    // they do not queue up behind the other waves' copies.
+    if (c > 0) copy(c - 1);
+    if (c == 0) {
+      // A4: hide keys past the causal diagonal or past the valid keys.
+      if constexpr (kMask) {
+        // Score i is key k0 + (i / 4) * 8 + half * 4 + i % 4: visible when
+        // (i / 4) * 8 + i % 4 is below lim.
+        const int lim = (kCausal ? min(kvlen, qrow + 1) : kvlen) - k0 - half * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = (i >> 2) * 8 + (i & 3) < lim ? sc[i] : kNegInf;
+      }
+      // A5: row max over this lane's 16 keys and its partner's 16, the new
+      // exponent reference (raised only past kLag) and alpha.
+      float mx = max3(sc[0], sc[1], sc[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mx = max3(mx, sc[i], sc[i + 1]);
+      mx = __builtin_fmaxf(mx, sc[15]);
+      mx = __builtin_fmaxf(mx, swap_halves(mx));
+      const float mt = mx * scale_log2;
+      m_new = mt > st.m_run + kLag ? mt : st.m_run;
+      ref = finite_ref(m_new);
+      alpha = exp2_hw(st.m_run - ref);
+    } else {
+      // P = 2^(S * scale * log2 e - ref).
+      const int lo = (c - 1) * 16 / kExpRegions, hi = c * 16 / kExpRegions;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i >= lo && i < hi) p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref));
+      }
+    }
+    if (c == kDC - 1) {
+      read_v(0);
+      read_v(1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.m_run = m_new;
+  // Keep the exponentials in phase 1: without this use the compiler sinks
+  // them past the rescale branch, next to the products that consume them.
+  asm volatile("" ::"v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]),
+               "v"(p[7]), "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]),
+               "v"(p[14]), "v"(p[15]));
 
-  // A6: rescale the accumulator (skipped when alpha is 1 on every lane),
-  // then O^T += V^T P^T.
+  // Phase 2 (A6): rescale the accumulator (skipped when alpha is 1 on every
+  // lane), then O^T += V^T P^T.
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
     // The empty asm keeps this a branch: without it the compiler would
     // multiply unconditionally, since scaling by 1 is harmless.
     asm volatile("");
 #pragma unroll
-    for (int b = 0; b < kDB; ++b) oacc[b] *= alpha;
+    for (int b = 0; b < kDB; ++b) st.oacc[b] *= alpha;
   }
-  // Transposed V reads: lane (group g = lane / 16, r = lane % 16) supplies the
-  // address of dims [d0 + 4 (r % 4), +4) of key row base + r / 4; it receives
-  // dims d0 + r of keys base .. base + 3 (d0 = 32 b + 16 (g % 2)).
+  // P in the B-operand layout: slice kc2 holds scores kc2 * 8 + 0..7, i.e.
+  // keys 16 kc2 + {0..3, 8..11} + 4 half, the order the V reads follow.
+  bf16x8 pb[2];
+  auto pack_p = [&](int kc2) {
+    const int o = kc2 * 8;
+    pb[kc2] = __builtin_bit_cast(
+        bf16x8, make_uint4(pack_bf16x2(p[o + 0], p[o + 1]), pack_bf16x2(p[o + 2], p[o + 3]),
+                           pack_bf16x2(p[o + 4], p[o + 5]), pack_bf16x2(p[o + 6], p[o + 7])));
+  };
+  pack_p(0);
+  float ps0 = 0.0f, ps1 = 0.0f;
+  constexpr int kAdds = 16 / kPV;  // scores summed per region
 #pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
+  for (int i = 0; i < kPV; ++i) {
+    const int kc2 = i / kDB, b = i % kDB;
+    if (i + 2 < kPV) read_v(i + 2);
+    if (i == 0) pack_p(1);
+    st.oacc[b] = mfma32(va[i % 3], pb[kc2], st.oacc[b]);
 #pragma unroll
-    for (int b = 0; b < kDB; ++b) {
-      const char* p0 = vbuf + off.v[b] + kc * 16 * kRow;
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(p0));
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(p0 + 8 * kRow));
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[b] = mfma32(a, pb[kc], oacc[b]);
+    for (int t = 0; t < kAdds; ++t) {
+      const int e = i * kAdds + t;
+      if (t & 1) ps1 += p[e]; else ps0 += p[e];
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // A3 for tile j + 1: its products follow this tile's in one stream.
-  if constexpr (kNext) compute_scores<D>(kbuf_next, off, qreg, snext);
+  st.l_run = st.l_run * alpha + (ps0 + ps1);
+  if constexpr (kNext) st.sc = sn;
 }
 
-// With kSplit, workgroup (head, query tile, split) covers only its share of
-// the key tiles and writes a partial result normalised by its own l -- O_s in
+// A sub-step of the last key tiles: skipped past the wave's last visible
+// sub-tile, always masked (these sub-tiles may cross the causal diagonal or
+// the key length).  It always forms the next scores, also on the wave's last
+// sub-tile, where they are not used: one code path keeps the register
+// allocation of the tail as simple as that of the main loop.
+template <int D, bool kCausal, int kKb, bool kBias, typename Copy>
+__device__ __forceinline__ void tail_sub_step(WaveState<D>& st, const char* kslot_next,
+                                              const char* vtile, const LaneOffsets<D>& off,
+                                              int s, int sw_last, int N, int kvlen, int qrow,
+                                              int half, float scale_log2, const float* brow,
+                                              const AttnOptions& opt, const Copy& copy) {
+  if (s > sw_last) {
+    // The wave still issues its share of the copies.
+#pragma unroll
+    for (int i = 0; i < D / 16 - 1; ++i) copy(i);
+    return;
+  }
+  sub_step<D, kCausal, kKb, true, true, kBias>(st, kslot_next, vtile, off, s, N, kvlen, qrow, half,
+                                               scale_log2, brow, opt, copy);
+}
+
+// Which (head, query tile) items a workgroup processes.
+//   kOnePerGroup: item = the workgroup's own id (split-K launches: one item
+//                 per workgroup, mapped by tile_of / tile_of_split).
+//   kPairsXcd:    a persistent grid, `workers` workgroups per XCD.  Items are
+//                 folded in pairs (query tiles p and nqt - 1 - p of one head,
+//                 so with a causal mask every pair holds the same number of
+//                 key tiles) and the pairs of the heads an XCD owns (bh = x
+//                 mod 8) are dealt round-robin to its workgroups: every
+//                 workgroup gets the same work, one head's pairs run side by
+//                 side on one XCD (its L2 holds that head's K and V), and no
+//                 workgroup waits to be dispatched behind a longer one.
+//   kPairsAll:    the same over all heads and the whole grid (B * H not a
+//                 multiple of 8).
+enum : int { kOnePerGroup = 0, kPairsXcd = 1, kPairsAll = 2 };
+
+struct Schedule {
+  int mode;
+  int nqt;            // query tiles per head
+  int pairs;          // pairs per head: ceil(nqt / 2)
+  int heads_per_xcd;  // kPairsXcd: B * H / 8
+  int workers;        // kPairsXcd: workgroups per XCD; kPairsAll: grid size
+};
+
+// Item k of workgroup g: returns 1 and sets (bh, qt, split), 0 when the
+// workgroup has no item k (nor any later one), -1 for an empty slot (the
+// second half of the middle pair when nqt is odd).
+__device__ __forceinline__ int item_of(const Schedule& sc, int g, int k, int BH, int splits,
+                                       bool causal, int& bh, int& qt, int& split) {
+  split = 0;
+  if (sc.mode == kOnePerGroup) {
+    if (k > 0) return 0;
+    if (splits > 1) {
+      tile_of_split(g, sc.nqt, splits, BH, causal, bh, qt, split);
+    } else {
+      tile_of(g, sc.nqt, BH, causal, bh, qt);
+    }
+    return 1;
+  }
+  int pi, p;
+  if (sc.mode == kPairsXcd) {
+    const int xcd = g & 7, w = g >> 3;
+    pi = w + (k >> 1) * sc.workers;
+    if (pi >= sc.heads_per_xcd * sc.pairs) return 0;
+    bh = (pi / sc.pairs) * 8 + xcd;
+    p = pi % sc.pairs;
+  } else {
+    pi = g + (k >> 1) * sc.workers;
+    if (pi >= BH * sc.pairs) return 0;
+    bh = pi / sc.pairs;
+    p = pi % sc.pairs;
+  }
+  const int heavy = sc.nqt - 1 - p;  // the query tile with more key tiles first
+  if (k & 1) {
+    if (p == heavy) return -1;
+    qt = p;
+  } else {
+    qt = heavy;
+  }
+  return 1;
+}
+
+// With kSplit, item (head, query tile, split) covers only its share of the
+// key tiles and writes a partial result normalised by its own l -- O_s in
 // float32 and LSE_s -- to o_part / lse_part; attn_split_merge_kernel combines
 // the splits.
 template <int D, bool kCausal, bool kBias, bool kSplit>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int BH,
-    int H, int N, float scale_log2, AttnOptions opt, int splits, float* __restrict__ o_part,
-    float* __restrict__ lse_part) {
+    int H, int N, float scale_log2, AttnOptions opt, Schedule sched, int splits,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
   using T = Tile<D>;
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
-  // Two K buffers and two V buffers: tile j's K sits in kbuf[j & 1], its V in
-  // vbuf[j & 1].
-  __shared__ __attribute__((aligned(1024))) char kbuf0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char kbuf1[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[T::kBytes];
+  constexpr int kSlot = 32 * D * 2;  // one 32-row K slot
+  // K streams through four 32-row slots (sub-tile t in slot t & 3); V through
+  // two 64-row buffers (tile j in buffer j & 1).  Each is its own array, and
+  // every copy into LDS names its target at compile time: the compiler then
+  // knows that a copy in flight does not alias the slots being read, and
+  // waits for it only at the barrier.
+  __shared__ __attribute__((aligned(1024))) char ks0[kSlot];
+  __shared__ __attribute__((aligned(1024))) char ks1[kSlot];
+  __shared__ __attribute__((aligned(1024))) char ks2[kSlot];
+  __shared__ __attribute__((aligned(1024))) char ks3[kSlot];
+  __shared__ __attribute__((aligned(1024))) char vb0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;   // the query row this lane works on (within the wave)
   const int half = lane >> 5;  // which 8-element half of each 16-wide slice
-
-  const int nqt = (N + kBM - 1) / kBM;
-  int bh, qt, split = 0;
-  if constexpr (kSplit) {
-    tile_of_split(blockIdx.x, nqt, splits, BH, kCausal, bh, qt, split);
-  } else {
-    tile_of(blockIdx.x, nqt, BH, kCausal, bh, qt);
-  }
-  const int64_t head_off = (int64_t)bh * N * D;
   const int head_bytes = N * D * 2;
-  const uint16_t* kh = k + head_off;
-  const uint16_t* vh = v + head_off;
-
-  const int q0 = qt * kBM;
-  const int qw = q0 + wave * 32;  // first query row of this wave
-  const int qrow = qw + col;      // this lane's query row
-  const int b = bh / H, h = bh % H;
-  const int kvlen = opt.kv_len ? min(max(opt.kv_len[b], 0), N) : N;
-  const float* brow = kBias ? opt.bias + b * opt.bias_stride_b + h * opt.bias_stride_h +
-                                  (int64_t)min(qrow, N - 1) * N
-                            : nullptr;
-
-  const int kv_end = kCausal ? min(kvlen, q0 + kBM) : kvlen;
-  const int ntiles_all = (kv_end + kBN - 1) / kBN;
-  // Key tiles [j_begin, j_end) of this workgroup (all of them without splits).
-  int j_begin = 0, j_end = ntiles_all;
-  if constexpr (kSplit) {
-    const int per = (ntiles_all + splits - 1) / splits;
-    j_begin = min(split * per, ntiles_all);
-    j_end = min(j_begin + per, ntiles_all);
-  }
-  const int ntiles = j_end - j_begin;
-  // Last key tile with work for this wave (below j_begin: none).
-  const int jw_last =
-      (qw >= N || ntiles == 0) ? -1 : (kCausal ? min(j_end - 1, (qw + 31) / kBN) : j_end - 1);
-
-  // A2 prologue: K and V of the first tile and K of the second in flight.
-  issue_tile<D, T::k_swz>(kbuf0, kh, head_bytes, j_begin * kBN, wave, lane);
-  issue_tile<D, T::v_swz>(vbuf0, vh, head_bytes, j_begin * kBN, wave, lane);
-  if (ntiles > 1) issue_tile<D, T::k_swz>(kbuf1, kh, head_bytes, (j_begin + 1) * kBN, wave, lane);
-
-  // A1: this lane's part of Q as the B operand of S^T = K Q^T.
-  bf16x8 qreg[kDC];
-  const uint16_t* qg = q + head_off + (int64_t)qrow * D + half * 8;
-#pragma unroll
-  for (int c = 0; c < kDC; ++c) {
-    qreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(qg + c * 16) : bf16x8{};
-  }
-
   const LaneOffsets<D> off = lane_offsets<D>(lane);
-  f32x16 oacc[kDB];
+  using KCopy = RowCopy<D, 32>;
+  using VCopy = RowCopy<D, 64>;
+  static_assert(2 * KCopy::kPerWave <= kDC - 1 && VCopy::kPerWave <= kDC - 1,
+                "a sub-step has a phase-1 region for each of its copies");
+  int koff[KCopy::kPerWave], voff[VCopy::kPerWave];
 #pragma unroll
-  for (int b = 0; b < kDB; ++b) oacc[b] = f32x16{};
-  float m_run = kNegInf;  // exponent reference, in units of log2(e) * scale * S
-  float l_run = 0.0f;     // this lane's half of the running sum
-  f32x16 sA[2], sB[2];    // scores of the current and the next tile
+  for (int i = 0; i < KCopy::kPerWave; ++i)
+    koff[i] = KCopy::template lane_offset<T::k_swz>(wave, lane, i);
+#pragma unroll
+  for (int i = 0; i < VCopy::kPerWave; ++i)
+    voff[i] = VCopy::template lane_offset<T::v_swz>(wave, lane, i);
+  WaveState<D> st;
 
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (jw_last >= j_begin) compute_scores<D>(kbuf0, off, qreg, sA);
+  for (int item = 0;; ++item) {
+    int bh, qt, split;
+    const int have = item_of(sched, blockIdx.x, item, BH, splits, kCausal, bh, qt, split);
+    if (have == 0) break;
+    if (have < 0) continue;
+    // Every wave is done with the LDS slots of the previous item.
+    if (item > 0) __syncthreads();
 
-  // A2: at the top of step j, K_{j+1} and V_j have landed and every wave is
-  // done with the buffers of K_j and V_{j-1}, which then receive K_{j+2} and
-  // V_{j+1}.  One barrier per key tile.
-  for (int j = j_begin; j < j_end; j += 2) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (j + 2 < j_end) issue_tile<D, T::k_swz>(kbuf0, kh, head_bytes, (j + 2) * kBN, wave, lane);
-    if (j + 1 < j_end) issue_tile<D, T::v_swz>(vbuf1, vh, head_bytes, (j + 1) * kBN, wave, lane);
-    if (j < jw_last) {
-      tile_step<D, kCausal, true, kBias>(kbuf1, vbuf0, off, j, N, kvlen, qw, qrow, half,
-                                         scale_log2, brow, opt, qreg, sA, sB, oacc, m_run, l_run);
-    } else if (j == jw_last) {
-      tile_step<D, kCausal, false, kBias>(kbuf1, vbuf0, off, j, N, kvlen, qw, qrow, half,
-                                          scale_log2, brow, opt, qreg, sA, sB, oacc, m_run, l_run);
-    }
-    if (j + 1 >= j_end) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (j + 3 < j_end) issue_tile<D, T::k_swz>(kbuf1, kh, head_bytes, (j + 3) * kBN, wave, lane);
-    if (j + 2 < j_end) issue_tile<D, T::v_swz>(vbuf0, vh, head_bytes, (j + 2) * kBN, wave, lane);
-    if (j + 1 < jw_last) {
-      tile_step<D, kCausal, true, kBias>(kbuf0, vbuf1, off, j + 1, N, kvlen, qw, qrow, half,
-                                         scale_log2, brow, opt, qreg, sB, sA, oacc, m_run, l_run);
-    } else if (j + 1 == jw_last) {
-      tile_step<D, kCausal, false, kBias>(kbuf0, vbuf1, off, j + 1, N, kvlen, qw, qrow, half,
-                                          scale_log2, brow, opt, qreg, sB, sA, oacc, m_run, l_run);
-    }
-  }
+    const int64_t head_off = (int64_t)bh * N * D;
+    const uint16_t* kh = k + head_off;
+    const uint16_t* vh = v + head_off;
+    const int q0 = qt * kBM;
+    const int qw = q0 + wave * 32;  // first query row of this wave
+    const int qrow = qw + col;      // this lane's query row
+    const int b = bh / H, h = bh % H;
+    const int kvlen = opt.kv_len ? min(max(opt.kv_len[b], 0), N) : N;
+    const float* brow = kBias ? opt.bias + b * opt.bias_stride_b + h * opt.bias_stride_h +
+                                    (int64_t)min(qrow, N - 1) * N
+                              : nullptr;
 
-  // A7: O = O / l (deferred division), LSE = ln 2 * (m + log2 l).
-  const float l_tot = l_run + swap_halves(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse_val = l_tot > 0.0f ? (finite_ref(m_run) + log2_hw(l_tot)) * kLn2 : kNegInf;
-  if (qrow < N) {
+    const int kv_end = kCausal ? min(kvlen, q0 + kBM) : kvlen;
+    const int ntiles_all = (kv_end + kBN - 1) / kBN;
+    // Key tiles [j_begin, j_end) of this item (all of them without splits).
+    int j_begin = 0, j_end = ntiles_all;
     if constexpr (kSplit) {
-      const int64_t prow = ((int64_t)split * BH + bh) * N + qrow;
-      float* orow = o_part + prow * D;
+      const int per = (ntiles_all + splits - 1) / splits;
+      j_begin = min(split * per, ntiles_all);
+      j_end = min(j_begin + per, ntiles_all);
+    }
+    // Last 32-key sub-tile with a visible key for this wave (below 2 j_begin:
+    // none).  Causal: the diagonal sub-tile, 32-aligned like the wave's rows.
+    int sw_last = min(2 * j_end, (kvlen + 31) / 32) - 1;
+    if constexpr (kCausal) sw_last = min(sw_last, qw / 32);
+    if (qw >= N || j_end <= j_begin) sw_last = -1;
+    const int s_end = 2 * j_end;
+    const int s0 = 2 * j_begin;
+
+    // Copies of 32-row K sub-tiles and 64-row V tiles; a sub-tile or tile
+    // outside this item's range becomes a zero fill (k0 = N).
+    auto copy_k = [&](char* slot, int t, int i) {
+      KCopy::issue(slot, kh, head_bytes, t < s_end ? t * 32 : N, wave, i, koff[i]);
+    };
+    auto copy_v = [&](char* buf, int jj, int i) {
+      VCopy::issue(buf, vh, head_bytes, jj < j_end ? jj * kBN : N, wave, i, voff[i]);
+    };
+
+    // A2 prologue: the first three K sub-tiles and the first V tile in flight.
 #pragma unroll
-      for (int b = 0; b < kDB; ++b) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const float4 w = make_float4(oacc[b][gq * 4 + 0] * inv, oacc[b][gq * 4 + 1] * inv,
-                                       oacc[b][gq * 4 + 2] * inv, oacc[b][gq * 4 + 3] * inv);
-          *reinterpret_cast<float4*>(orow + b * 32 + gq * 8 + half * 4) = w;
-        }
+    for (int i = 0; i < KCopy::kPerWave; ++i) {
+      if ((j_begin & 1) == 0) {
+        copy_k(ks0, s0, i);
+        copy_k(ks1, s0 + 1, i);
+        copy_k(ks2, s0 + 2, i);
+      } else {
+        copy_k(ks2, s0, i);
+        copy_k(ks3, s0 + 1, i);
+        copy_k(ks0, s0 + 2, i);
       }
-      if (half == 0) lse_part[prow] = lse_val;
-    } else {
-      uint16_t* orow = o + head_off + (int64_t)qrow * D;
+    }
 #pragma unroll
-      for (int b = 0; b < kDB; ++b) {
+    for (int i = 0; i < VCopy::kPerWave; ++i) {
+      if ((j_begin & 1) == 0) copy_v(vb0, j_begin, i); else copy_v(vb1, j_begin, i);
+    }
+
+    // A1: this lane's part of Q as the B operand of S^T = K Q^T.
+    const uint16_t* qg = q + head_off + (int64_t)qrow * D + half * 8;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          // O^T rows b*32 + gq*8 + half*4 + (0..3): four consecutive dims.
-          uint2 w;
-          w.x = pack_bf16x2(oacc[b][gq * 4 + 0] * inv, oacc[b][gq * 4 + 1] * inv);
-          w.y = pack_bf16x2(oacc[b][gq * 4 + 2] * inv, oacc[b][gq * 4 + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + b * 32 + gq * 8 + half * 4) = w;
-        }
+    for (int c = 0; c < kDC; ++c) {
+      st.qreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(qg + c * 16) : bf16x8{};
+    }
+#pragma unroll
+    for (int i = 0; i < kDB; ++i) st.oacc[i] = f32x16{};
+    st.m_run = kNegInf;
+    st.l_run = 0.0f;
+    st.sc = f32x16{};
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (sw_last >= s0) st.sc = sub_scores<D>((j_begin & 1) ? ks2 : ks0, off, st.qreg);
+
+    // A2: at the top of the step for tile j, K sub-tiles 2j + 1 and 2j + 2
+    // and V_j have landed and every wave is done with sub-tiles 2j - 1 and 2j
+    // and with V_{j-1}, whose places receive sub-tiles 2j + 3, 2j + 4 (copied
+    // during the tile's first sub-step) and V_{j+1} (during its second).  One
+    // barrier per 64-key tile.  Tile j even: its sub-tiles read the next
+    // scores from slots 1 and 2 and V from buffer 0; j odd: slots 3, 0 and
+    // buffer 1.
+#define OSM_TILE_COPIES(J, ODD)                                                               \
+  auto cp0 = [&](int i) {                                                                     \
+    if (i < KCopy::kPerWave)                                                                  \
+      copy_k(ODD ? ks1 : ks3, 2 * (J) + 3, i);                                                \
+    else if (i < 2 * KCopy::kPerWave)                                                         \
+      copy_k(ODD ? ks2 : ks0, 2 * (J) + 4, i - KCopy::kPerWave);                              \
+  };                                                                                          \
+  auto cp1 = [&](int i) {                                                                     \
+    if (i < VCopy::kPerWave) copy_v(ODD ? vb0 : vb1, (J) + 1, i);                             \
+  }
+    // Main part: tiles that no wave masks (keys below the item's first query
+    // row when causal, whole tiles below the key length) and whose sub-tiles
+    // are all followed by another for every wave: one code path.
+#define OSM_MAIN_TILE(J, ODD)                                                                 \
+  do {                                                                                        \
+    __builtin_amdgcn_s_waitcnt(0);                                                            \
+    __syncthreads();                                                                          \
+    OSM_TILE_COPIES(J, ODD);                                                                  \
+    sub_step<D, kCausal, 0, true, false, kBias>(st, ODD ? ks3 : ks1, ODD ? vb1 : vb0, off,    \
+                                                2 * (J), N, kvlen, qrow, half, scale_log2,    \
+                                                brow, opt, cp0);                              \
+    sub_step<D, kCausal, 1, true, false, kBias>(st, ODD ? ks0 : ks2, ODD ? vb1 : vb0, off,    \
+                                                2 * (J) + 1, N, kvlen, qrow, half,            \
+                                                scale_log2, brow, opt, cp1);                  \
+  } while (0)
+    // The last tiles (those crossing the diagonal or the key length, and the
+    // final one), with per-wave choices.
+#define OSM_TAIL_TILE(J, ODD)                                                                 \
+  do {                                                                                        \
+    __builtin_amdgcn_s_waitcnt(0);                                                            \
+    __syncthreads();                                                                          \
+    OSM_TILE_COPIES(J, ODD);                                                                  \
+    tail_sub_step<D, kCausal, 0, kBias>(st, ODD ? ks3 : ks1, ODD ? vb1 : vb0, off, 2 * (J),   \
+                                        sw_last, N, kvlen, qrow, half, scale_log2, brow, opt, \
+                                        cp0);                                                 \
+    tail_sub_step<D, kCausal, 1, kBias>(st, ODD ? ks0 : ks2, ODD ? vb1 : vb0, off,            \
+                                        2 * (J) + 1, sw_last, N, kvlen, qrow, half,           \
+                                        scale_log2, brow, opt, cp1);                          \
+  } while (0)
+
+    int full_end = min(j_end, kvlen / kBN);
+    if constexpr (kCausal) full_end = min(full_end, q0 / kBN);
+    const int main_end = max(j_begin, min(full_end, j_end - 1));
+    int j = j_begin;
+    if ((j & 1) && j < main_end) {
+      OSM_MAIN_TILE(j, true);
+      ++j;
+    }
+    for (; j + 1 < main_end; j += 2) {
+      OSM_MAIN_TILE(j, false);
+      OSM_MAIN_TILE(j + 1, true);
+    }
+    if (j < main_end) {
+      OSM_MAIN_TILE(j, false);
+      ++j;
+    }
+    for (; j < j_end; ++j) {
+      if (j & 1) {
+        OSM_TAIL_TILE(j, true);
+      } else {
+        OSM_TAIL_TILE(j, false);
       }
-      if (half == 0) lse[(int64_t)bh * N + qrow] = lse_val;
+    }
+#undef OSM_TAIL_TILE
+#undef OSM_MAIN_TILE
+#undef OSM_TILE_COPIES
+
+    // A7: O = O / l (deferred division), LSE = ln 2 * (m + log2 l).  The
+    // stores are not waited for: the next item's loads go out behind them.
+    const float l_tot = st.l_run + swap_halves(st.l_run);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse_val = l_tot > 0.0f ? (finite_ref(st.m_run) + log2_hw(l_tot)) * kLn2 : kNegInf;
+    if (qrow < N) {
+      if constexpr (kSplit) {
+        const int64_t prow = ((int64_t)split * BH + bh) * N + qrow;
+        float* orow = o_part + prow * D;
+#pragma unroll
+        for (int bb = 0; bb < kDB; ++bb) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x16& oa = st.oacc[bb];
+            const float4 w = make_float4(oa[gq * 4 + 0] * inv, oa[gq * 4 + 1] * inv,
+                                         oa[gq * 4 + 2] * inv, oa[gq * 4 + 3] * inv);
+            *reinterpret_cast<float4*>(orow + bb * 32 + gq * 8 + half * 4) = w;
+          }
+        }
+        if (half == 0) lse_part[prow] = lse_val;
+      } else {
+        uint16_t* orow = o + head_off + (int64_t)qrow * D;
+#pragma unroll
+        for (int bb = 0; bb < kDB; ++bb) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            // O^T rows bb*32 + gq*8 + half*4 + (0..3): four consecutive dims.
+            const f32x16& oa = st.oacc[bb];
+            uint2 w;
+            w.x = pack_bf16x2(oa[gq * 4 + 0] * inv, oa[gq * 4 + 1] * inv);
+            w.y = pack_bf16x2(oa[gq * 4 + 2] * inv, oa[gq * 4 + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + bb * 32 + gq * 8 + half * 4) = w;
+          }
+        }
+        if (half == 0) lse[(int64_t)bh * N + qrow] = lse_val;
+      }
     }
   }
 }
@@ -516,17 +746,56 @@ __global__ __launch_bounds__(256) void attn_split_merge_kernel(const float* __re
   if (dq == 0) lse[row] = L > 0.0f ? M + log2_hw(L) * kLn2 : kNegInf;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int D, bool kCausal, bool kBias, bool kSplit>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int H,
                   int N, float scale, const AttnOptions& opt, int splits, float* o_part,
                   float* lse_part, hipStream_t s) {
   const int nqt = (N + kBM - 1) / kBM;
   const float scale_log2 = scale * kLog2e;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, kCausal, kBias, kSplit>),
-                     dim3(nqt * BH * (kSplit ? splits : 1)), dim3(kThreads), 0, s,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, H, N,
-                     scale_log2, opt, splits, o_part, lse_part);
+  Schedule sc;
+  sc.nqt = nqt;
+  sc.pairs = (nqt + 1) / 2;
+  sc.heads_per_xcd = BH / 8;
+  int64_t grid;
+  if (kSplit) {
+    sc.mode = kOnePerGroup;
+    sc.workers = 0;
+    grid = (int64_t)nqt * BH * splits;
+  } else {
+    // Two resident workgroups per compute unit.
+    const int slots = 2 * device_cus();
+    if ((BH & 7) == 0 && slots >= 8) {
+      sc.mode = kPairsXcd;
+      const int64_t per_xcd = (int64_t)sc.heads_per_xcd * sc.pairs;
+      sc.workers = (int)(per_xcd < slots / 8 ? per_xcd : slots / 8);
+      grid = 8 * (int64_t)sc.workers;
+    } else {
+      sc.mode = kPairsAll;
+      const int64_t total = (int64_t)BH * sc.pairs;
+      sc.workers = (int)(total < slots ? total : slots);
+      grid = sc.workers;
+    }
+  }
+  hipLaunchKernelGGL((attn_fwd_kernel<D, kCausal, kBias, kSplit>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     static_cast<uint16_t*>(o), lse, BH, H, N, scale_log2, opt, sc, splits, o_part,
+                     lse_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !kSplit) return e;
   const int64_t rows = (int64_t)BH * N;
