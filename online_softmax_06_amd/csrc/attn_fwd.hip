@@ -88,10 +88,10 @@ struct Tile {
 // Global->LDS copy of kRows key rows [k0, k0 + kRows) of K or V into `buf`
 // (row-major, 16-byte units XOR-swizzled by `Swz`), one instruction at a
 // time: instruction i of wave w fills LDS units [(w * kPerWave + i) * 64,
-// +64), one 16-byte unit per lane.  The key offset goes in the scalar offset,
-// the lane's part in a loop-invariant vector offset.  Keys at or past the end
-// of the head (the descriptor's range) read as zeros; k0 = N therefore turns
-// an instruction into a harmless zero fill without memory traffic.
+// +64), one 16-byte unit per lane at a loop-invariant per-lane offset.  The
+// buffer descriptor starts at row k0 and ends with the head, so rows at or
+// past the end of the head fall outside its range and arrive as zeros; k0 =
+// N turns an instruction into a zero fill without memory traffic.
 template <int D, int kRows>
 struct RowCopy {
   static constexpr int kUnits = D / 8;
@@ -108,9 +108,11 @@ struct RowCopy {
     // The buffer-to-LDS builtins exist only for the device; the host pass of
     // this single-source file sees an empty body.
 #if defined(__HIP_DEVICE_COMPILE__)
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, head_bytes, kBufferFlags);
+    const int left = head_bytes - k0 * (D * 2);
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)k0 * D), 0,
+                                                        left > 0 ? left : 0, kBufferFlags);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, OSM_LDS(buf + (wave * kPerWave + i) * 1024), 16,
-                                             voff, k0 * (D * 2), 0, 0);
+                                             voff, 0, 0, 0);
 #endif
   }
 };

@@ -137,3 +137,25 @@ def test_large_configs_sampled_heads(name, count, must):
     os_, ls = sel(o), torch.stack([lse[b, h] for b, h in heads])[:, None]
     eo, el = compare(qs, ks, vs, cfg["scale"], cfg["causal"], os_, ls)
     print(f"[result] {name} heads {heads} O err {eo:.3g} LSE err {el:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_no_reads_past_the_head(D, causal):
+    # K and V are followed in their allocation by NaN: a copy that read key
+    # rows past N would bring NaN into the products (0 * NaN is NaN).
+    B, H, N = 1, 2, 100
+    _announce("NaN past the end", B, H, N, D, causal)
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=31, device="cuda")
+    pad = 64 * 128
+    kb = torch.full((k.numel() + pad,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vb = torch.full((v.numel() + pad,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kb[:k.numel()].copy_(k.flatten())
+    vb[:v.numel()].copy_(v.flatten())
+    kk = kb[:k.numel()].view(B, H, N, D)
+    vv = vb[:v.numel()].view(B, H, N, D)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = osm.attn_fwd(q, kk, vv, scale, causal)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    compare(q, k, v, scale, causal, o, lse)
