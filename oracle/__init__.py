@@ -25,6 +25,10 @@ online_ref     the element-wise online normaliser and the (m, l) combine
 attention_ref  materialised-S attention with log-sum-exp ([Ch6 §6.5],
                [Ch6 §6.6], [xxqk §4.2]) and the single-query blocked alpha/beta
                form ([Ch6 §6.6]) as a self-check.
+attention_bwd_ref
+               gradients dQ, dK, dV of that attention through the softmax
+               Jacobian (the backward that [Ch6 §6.5] and [xxqk §5.2] say
+               recomputes S from the saved log-sum-exp).
 
 The oracle shares no code with the HIP library and never imports it.  Pins that
 tie it to something other than itself live in ``tests/test_oracle_*.py``.
@@ -34,6 +38,7 @@ Parity status of each function is stated in its docstring.
 from .softmax_ref import masked_softmax_rows_ref, naive_softmax_rows_f32, softmax_rows_ref
 from .online_ref import EMPTY_STATE, all_trees, combine, online_state, tree_reduce
 from .attention_ref import attention_head_ref, attention_ref, blocked_attention_row_ref
+from .attention_bwd_ref import attention_bwd_head_ref, attention_bwd_ref, attention_probs_head_ref
 
 __all__ = [
     "softmax_rows_ref",
@@ -47,4 +52,7 @@ __all__ = [
     "attention_head_ref",
     "attention_ref",
     "blocked_attention_row_ref",
+    "attention_probs_head_ref",
+    "attention_bwd_head_ref",
+    "attention_bwd_ref",
 ]

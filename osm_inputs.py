@@ -20,6 +20,9 @@ Workloads (sizes and value distributions of the five standard configurations):
 5. ``attn_long``: B=1, H=32, N=16384, D=128, causal, Q, K ~ 1.5*N(0,1),
    V ~ N(0,1); scale = float32(1/sqrt(128)).
 
+Attention backward: the same Q, K, V plus an upstream gradient dO ~ N(0,1)
+in bfloat16, drawn from its own generator seeded with 1000 + the seed.
+
 "N(mu, sigma)" is read with sigma the standard deviation.  Seeds are the
 configuration number (1-5).  Random draws are float32 from a torch generator
 on the requested device, in a fixed order; bfloat16 tensors are round-to-nearest
@@ -100,6 +103,13 @@ def attention_inputs(B, H, N, D, seed, qk_sigma=1.0, v_sigma=1.0, device="cpu"):
     k = (qk_sigma * torch.randn(shape, generator=g, device=device)).to(torch.bfloat16)
     v = (v_sigma * torch.randn(shape, generator=g, device=device)).to(torch.bfloat16)
     return q, k, v
+
+
+def attention_grad_output(B, H, N, D, seed, device="cpu"):
+    """Upstream gradient dO of shape [B, H, N, D], N(0,1) in bfloat16, from its
+    own generator (seed 1000 + seed), so Q, K, V are unchanged by drawing it."""
+    g = generator(1000 + int(seed), device)
+    return torch.randn((B, H, N, D), generator=g, device=device).to(torch.bfloat16)
 
 
 def attention_config(name, device="cpu", **override):
