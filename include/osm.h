@@ -221,6 +221,48 @@ int osm_attn_fwd_split(const void* q, const void* k, const void* v, void* o, flo
  * -1 for invalid arguments. */
 int64_t osm_attn_fwd_split_workspace(int B, int H, int N, int D, int splits);
 
+/*
+ * osm_attn_bwd -- attention backward from the forward's output and
+ * log-sum-exp, with the scores recomputed instead of stored ([Ch6 §6.5]: the
+ * forward keeps one LSE per row for the backward; [xxqk §5.2]: the backward
+ * recomputes S, trading compute for memory).
+ *
+ * For O = softmax(S) V with S as in osm_attn_fwd (scale, optional causal
+ * mask) and an upstream gradient dO, with P = exp(S - LSE):
+ *   dv = P^T dO
+ *   dS = P * (dO V^T - Delta),   Delta[i] = dot(dO[i, :], O[i, :])
+ *   dq = scale * dS K,   dk = scale * dS^T Q
+ * per batch and head.  P and dS enter the products as bfloat16, products
+ * accumulate in float32, Delta is formed in float32 from o and dout.
+ *
+ *   q, k, v     device pointers, contiguous [B, H, N, D] bfloat16 (the
+ *               forward's inputs).
+ *   o, lse      the forward's outputs for these inputs, same scale and causal
+ *               flag: o [B, H, N, D] bfloat16, lse [B, H, N] float32 (a row
+ *               with lse = -inf contributes nothing).
+ *   dout        device pointer, [B, H, N, D] bfloat16: dL/do.
+ *   dq, dk, dv  device pointers, [B, H, N, D] bfloat16, written (rounded to
+ *               nearest even).  They must not overlap each other, any input
+ *               or the workspace.
+ *   B, H, N, D, scale, causal   as osm_attn_fwd.
+ *   workspace   device memory owned by the caller, 16-byte aligned, at least
+ *               osm_attn_bwd_workspace(B, H, N, D) bytes; its content on
+ *               entry does not matter.  Calls that share a workspace must be
+ *               ordered (same stream).
+ *   stream      hipStream_t to enqueue on (three kernels, in order).
+ *
+ * The result does not depend on the launch (no atomics): equal inputs give
+ * bitwise equal gradients.  Returns as osm_attn_fwd, plus OSM_ERR_INVALID_ARG
+ * for a missing, misaligned or too small workspace.
+ */
+int osm_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int D,
+                 float scale, int causal, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace osm_attn_bwd needs: 8 * B * H * (N rounded up to a
+ * multiple of 128); -1 for invalid arguments. */
+int64_t osm_attn_bwd_workspace(int B, int H, int N, int D);
+
 /* Human-readable name of a status code; never NULL, static storage. */
 const char* osm_status_string(int status);
 

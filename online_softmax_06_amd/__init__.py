@@ -20,6 +20,9 @@ ints; ``stream`` is a hipStream_t handle, 0 for the null stream):
                        bias_stride_b, bias_stride_h, splits, workspace,
                        workspace_bytes, stream) -> status
     osm_attn_fwd_split_workspace(B, H, N, D, splits) -> bytes
+    osm_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale, causal,
+                 workspace, workspace_bytes, stream) -> status
+    osm_attn_bwd_workspace(B, H, N, D) -> bytes
     osm_status_string(status) -> str
 
 Tensor-level helpers:
@@ -27,6 +30,7 @@ Tensor-level helpers:
     softmax_rows(x, out=None, mask=None, row_len=None, split=False) -> Tensor
     attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None,
              kv_len=None, bias=None, splits=1) -> (o, lse)
+    attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False) -> (dq, dk, dv)
 
 If the library has not been built, every call raises ``RuntimeError``; there
 is no fallback implementation.
@@ -41,8 +45,9 @@ __all__ = [
     "OsmError", "lib_path", "load_library", "osm_softmax_rows", "osm_softmax_rows_ex",
     "osm_softmax_rows_split", "osm_softmax_rows_split_workspace",
     "osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split", "osm_attn_fwd_split_workspace",
+    "osm_attn_bwd", "osm_attn_bwd_workspace",
     "osm_status_string", "osm_version", "softmax_rows",
-    "attn_fwd",
+    "attn_fwd", "attn_bwd",
 ]
 
 OSM_F32, OSM_BF16 = 0, 1
@@ -97,6 +102,11 @@ def load_library():
     lib.osm_attn_fwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_f,
                                  c_int, c_vp]
     lib.osm_attn_fwd.restype = c_int
+    lib.osm_attn_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int,
+                                 c_int, c_int, c_int, c_f, c_int, c_vp, c_i64, c_vp]
+    lib.osm_attn_bwd.restype = c_int
+    lib.osm_attn_bwd_workspace.argtypes = [c_int, c_int, c_int, c_int]
+    lib.osm_attn_bwd_workspace.restype = c_i64
     lib.osm_status_string.argtypes = [c_int]
     lib.osm_status_string.restype = ctypes.c_char_p
     lib.osm_version.argtypes = []
@@ -151,6 +161,16 @@ def osm_attn_fwd_split(q, k, v, o, lse, B, H, N, D, scale, causal, kv_len, bias,
 
 def osm_attn_fwd_split_workspace(B, H, N, D, splits):
     return load_library().osm_attn_fwd_split_workspace(B, H, N, D, splits)
+
+
+def osm_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale, causal, workspace,
+                 workspace_bytes, stream=0):
+    return load_library().osm_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
+                                       int(causal), workspace, workspace_bytes, stream)
+
+
+def osm_attn_bwd_workspace(B, H, N, D):
+    return load_library().osm_attn_bwd_workspace(B, H, N, D)
 
 
 def osm_status_string(status):
@@ -295,3 +315,43 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None,
     if st != OSM_OK:
         raise OsmError(st, "osm_attn_fwd_ex")
     return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None):
+    """Attention backward on contiguous bfloat16 [B, H, N, D] CUDA tensors.
+
+    ``o`` and ``lse`` are the forward's outputs for ``q, k, v`` with the same
+    ``scale`` and ``causal``; ``dout`` is the gradient of the loss with respect
+    to ``o``.  Returns ``(dq, dk, dv)`` (bfloat16, shaped like q).  The
+    workspace is allocated here, through torch's caching allocator.
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor [B, H, N, D]")
+        if t.shape != q.shape:
+            raise ValueError("q, k, v, o and dout must have the same shape [B, H, N, D]")
+    B, H, N, D = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 CUDA tensor [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    grads = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        elif t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor shaped like q")
+        grads.append(t)
+    need = osm_attn_bwd_workspace(B, H, N, D)
+    if need < 0:
+        raise OsmError(OSM_ERR_INVALID_ARG, "osm_attn_bwd_workspace")
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = osm_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                      grads[2].data_ptr(), B, H, N, D, float(scale), bool(causal),
+                      ws.data_ptr(), ws.numel(), _stream_handle(q.device))
+    if st != OSM_OK:
+        raise OsmError(st, "osm_attn_bwd")
+    return tuple(grads)

@@ -1,0 +1,577 @@
+// Fused attention backward on gfx950: dQ, dK, dV of O = softmax(scale Q K^T) V
+// from Q, K, V, the output O, its per-row log-sum-exp and the upstream
+// gradient dO, with the scores recomputed on the matrix cores and no N x N
+// matrix in HBM.
+//
+// Method.  The forward keeps only O and one log-sum-exp per query row
+// ("Ch.6 Softmax and Online Softmax" §6.5), and the backward rebuilds the
+// probabilities from them instead of reading a stored S (xxqk §5.2: compute
+// traded for memory):  P = 2^(S' - LSE log2 e) with S' = S * scale * log2 e,
+// which is the normalised softmax without any running max.  The gradients are
+// those of the forward map:
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - Delta),   Delta_i = sum_j P_ij dP_ij,
+//     dQ = scale dS K,   dK = scale dS^T Q,
+// with Delta_i computed as the row dot product dO_i . O_i (equal to the sum
+// above because O_i = sum_j P_ij V_j), so it costs one pass over O and dO.
+//
+// Three launches, no atomics (the result is deterministic):
+//   prep  Delta and LSE * log2 e per query row into a padded workspace
+//         (padding rows get Delta = 0 and +inf, so their P is exactly 0);
+//   dkdv  a workgroup owns 128 keys (32 per wavefront), keeps their K and V
+//         fragments and the dK^T, dV^T accumulators in registers and streams
+//         the 64-row tiles of Q and dO (plus their Delta and LSE) through
+//         LDS: per 32-row sub-tile S = Q K^T, dP = dO V^T, P, dS, then
+//         dV^T += dO^T P and dK^T += Q^T dS;
+//   dq    a workgroup owns 128 query rows (32 per wavefront), keeps Q, dO,
+//         Delta, LSE and the dQ^T accumulator in registers and streams the
+//         64-key tiles of K and V: S^T = K Q^T, dP^T = V dO^T, P, dS, then
+//         dQ^T += K^T dS^T.
+// The second kernel repeats two of the first kernel's products (the scores
+// and dP) instead of adding partial dQ into HBM with atomics.
+//
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64).  A product whose
+// output has lanes = the index kept by the wavefront and registers = the
+// streamed index feeds the next product directly as its B operand, when that
+// product contracts over the streamed index.  The streamed tiles are read
+// twice: row-wise (16 bytes per lane, A operand of the first products) and
+// transposed (ds_read_b64_tr_b16, A operand of the accumulating products).
+// One XOR swizzle of the 16-byte units serves both reads without bank
+// conflicts (see Geo::swz).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "osm_device.h"
+#include "osm_internal.h"
+
+namespace osm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBlk = 128;  // keys per dK/dV workgroup; query rows per dQ workgroup
+constexpr int kTile = 64;  // rows of a streamed tile (query rows or keys)
+constexpr int kPad = 128;  // per-head row padding of the Delta / LSE arrays
+
+// Buffer descriptor word 3 for raw (untyped) buffer loads on gfx950.
+constexpr int kBufferFlags = 0x00020000;
+
+#define OSM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Geometry of a streamed tile of kTile rows x D bfloat16, row-major in LDS.
+template <int D>
+struct Geo {
+  static constexpr int kUnits = D / 8;     // 16-byte units per row
+  static constexpr int kRow = D * 2;       // bytes per row
+  static constexpr int kBytes = kTile * kRow;
+  static constexpr int kDC = D / 16;       // 16-wide slices of the head dimension
+  static constexpr int kDB = D / 32;       // 32-wide blocks of the head dimension
+  static constexpr int kCopies = kTile * kUnits / 64 / kWaves;  // 16-byte copies per lane
+  // Unit u of row r sits at unit u ^ swz(r).
+  //  * Row reads: 16 lanes read one unit of 16 consecutive rows; swz takes 16
+  //    distinct values on them (D = 128: 16 units per 256-byte row) or 8
+  //    distinct values on the rows of each parity (D = 64: two rows per
+  //    256-byte bank sweep), so the 16 units hit disjoint banks.
+  //  * Transposed reads: 32 lanes read 64 contiguous bytes of 4 consecutive
+  //    rows; swz moves the four rows to four different 64-byte quarters of
+  //    the bank space.
+  // Rows r and r + 8 differ by kPartXor in their byte offset.
+  __device__ static int swz(int r) {
+    if constexpr (D == 128) return (((r & 3) << 2) | ((r & 4) >> 1)) ^ ((r >> 3) & 1);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+  static constexpr int kPartXor = D == 128 ? 16 : 32;
+};
+
+// Global->LDS copy of rows [row0, row0 + kTile) of one head (row-major,
+// D bfloat16 per row) into `lds`, swizzled: copy i of wave w fills LDS bytes
+// [(w * kCopies + i) * 1024, +1024), one 16-byte unit per lane at the per-lane
+// source offset `off[i]`.  The buffer descriptor starts at row0 and ends with
+// the head, so rows past the head arrive as zeros.
+template <int D>
+__device__ __forceinline__ void copy_rows(char* lds, const uint16_t* head, int head_bytes,
+                                          int row0, int wave, const int (&off)[Geo<D>::kCopies]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int left = head_bytes - row0 * Geo<D>::kRow;
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(head + (int64_t)row0 * D), 0,
+                                                      left > 0 ? left : 0, kBufferFlags);
+#pragma unroll
+  for (int i = 0; i < Geo<D>::kCopies; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, OSM_LDS(lds + (wave * Geo<D>::kCopies + i) * 1024),
+                                             16, off[i], 0, 0, 0);
+#endif
+}
+
+// Global->LDS copy of 64 floats (one per lane) starting at `src`.
+__device__ __forceinline__ void copy_vec64(float* lds, const float* src, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, 64 * 4, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, OSM_LDS(lds), 4, lane * 4, 0, 0, 0);
+#endif
+}
+
+// Per-lane LDS byte offsets for the two reads of a streamed tile.
+//   row: lane reads row (lane % 32) of a 32-row sub-tile, unit 2 c + half of
+//        slice c at offset row ^ (c << 5).
+//   tr[b]: transposed read of dim block b: lane (g = lane / 16, r = lane % 16)
+//        supplies the address of dims [32 b + 16 (g % 2) + 4 (r % 4), +4) of
+//        row 4 half + r / 4 of a 16-row slice (rows +8 for the second read of
+//        the slice) and receives dim 32 b + lane % 32 of four consecutive rows.
+template <int D>
+struct ReadOffsets {
+  int row;
+  int tr[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ ReadOffsets<D> read_offsets(int lane) {
+  using G = Geo<D>;
+  const int col = lane & 31, half = lane >> 5;
+  ReadOffsets<D> o;
+  o.row = col * G::kRow + ((half ^ G::swz(col)) << 4);
+  const int g = lane >> 4, r = lane & 15;
+  const int trow = half * 4 + (r >> 2);
+  const int td = (g & 1) * 16 + 4 * (r & 3);
+#pragma unroll
+  for (int b = 0; b < G::kDB; ++b) {
+    const int d = b * 32 + td;
+    o.tr[b] = trow * G::kRow + (((d >> 3) ^ G::swz(trow)) << 4) + (d & 7) * 2;
+  }
+  return o;
+}
+
+// A operand of an accumulating product: dims [32 b, +32) x rows
+// {r0 + 4 half + 0..3, r0 + 8 + 4 half + 0..3} of a streamed tile (r0 a
+// multiple of 16), transposed; the row order is the register order of a
+// 32 x 32 product output, so P and dS enter as B operands unchanged.
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr(const char* tile, const ReadOffsets<D>& off, int b,
+                                          int r0) {
+  using G = Geo<D>;
+  const int o0 = off.tr[b] + r0 * G::kRow;
+  const int o1 = (o0 + 8 * G::kRow) ^ G::kPartXor;
+  const s16x4 v0 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + o0));
+  const s16x4 v1 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + o1));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A operand of a first product: rows [r0, r0 + 32) of a streamed tile, slice c.
+template <int D>
+__device__ __forceinline__ bf16x8 read_row(const char* tile, const ReadOffsets<D>& off, int c,
+                                           int r0) {
+  return *reinterpret_cast<const bf16x8*>(tile + r0 * Geo<D>::kRow + (off.row ^ (c << 5)));
+}
+
+// Registers 8 kc2 .. 8 kc2 + 7 of a 32 x 32 product output, as a bfloat16
+// B operand.
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[16], int kc2) {
+  const int o = kc2 * 8;
+  return __builtin_bit_cast(
+      bf16x8, make_uint4(pack_bf16x2(x[o + 0], x[o + 1]), pack_bf16x2(x[o + 2], x[o + 3]),
+                         pack_bf16x2(x[o + 4], x[o + 5]), pack_bf16x2(x[o + 6], x[o + 7])));
+}
+
+// Output register i of a 32 x 32 product sits in row rho(i) + 4 half.
+__device__ __forceinline__ constexpr int rho(int i) { return (i >> 2) * 8 + (i & 3); }
+
+// Map a linear workgroup id to (batch*head, block).  Workgroups go
+// round-robin over the 8 XCDs; when B*H is a multiple of 8, all blocks of one
+// head land on one XCD, whose L2 then holds the head's streamed tiles.
+__device__ __forceinline__ void block_of(int L, int per_head, int BH, int& bh, int& rank) {
+  if ((BH & 7) == 0) {
+    const int xcd = L & 7, idx = L >> 3;
+    bh = (idx / per_head) * 8 + xcd;
+    rank = idx % per_head;
+  } else {
+    bh = L / per_head;
+    rank = L % per_head;
+  }
+}
+
+// Store 4 consecutive floats times `mul` as bfloat16 (8 bytes).
+__device__ __forceinline__ void store4(uint16_t* dst, const f32x16& a, int i0, float mul) {
+  *reinterpret_cast<uint2*>(dst) =
+      make_uint2(pack_bf16x2(a[i0] * mul, a[i0 + 1] * mul), pack_bf16x2(a[i0 + 2] * mul, a[i0 + 3] * mul));
+}
+
+// ---------------------------------------------------------------------------
+// prep: Delta_i = dO_i . O_i and LSE_i * log2 e per query row, over the padded
+// range [0, Np) of every head.  D / 8 lanes share a row, 8 elements each.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ delta, float* __restrict__ lse2, int BH, int N, int Np) {
+  constexpr int kLanes = D / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / kLanes;  // over BH * Np
+  const int part = (int)(t % kLanes);
+  const int64_t bh = row / Np;
+  const int i = (int)(row % Np);
+  float acc = 0.0f;
+  if (bh < BH && i < N) {
+    const int64_t e = (bh * N + i) * D + part * 8;
+    const uint4 a = *reinterpret_cast<const uint4*>(o + e);
+    const uint4 g = *reinterpret_cast<const uint4*>(dout + e);
+    acc = bf16_lo(a.x) * bf16_lo(g.x);
+    acc = __builtin_fmaf(bf16_hi(a.x), bf16_hi(g.x), acc);
+    acc = __builtin_fmaf(bf16_lo(a.y), bf16_lo(g.y), acc);
+    acc = __builtin_fmaf(bf16_hi(a.y), bf16_hi(g.y), acc);
+    acc = __builtin_fmaf(bf16_lo(a.z), bf16_lo(g.z), acc);
+    acc = __builtin_fmaf(bf16_hi(a.z), bf16_hi(g.z), acc);
+    acc = __builtin_fmaf(bf16_lo(a.w), bf16_lo(g.w), acc);
+    acc = __builtin_fmaf(bf16_hi(a.w), bf16_hi(g.w), acc);
+  }
+#pragma unroll
+  for (int m = 1; m < kLanes; m <<= 1) acc += __shfl_xor(acc, m, kLanes);
+  if (part == 0 && bh < BH) {
+    delta[row] = acc;
+    const float l = i < N ? lse[bh * N + i] : kNegInf;
+    // A row without a visible key (LSE = -inf) and a padding row get +inf:
+    // every P of the row is then 2^-inf = 0.
+    lse2[row] = l == kNegInf ? __builtin_inff() : l * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dkdv: dK and dV of 128 keys per workgroup.
+// ---------------------------------------------------------------------------
+template <int D, bool kCausal>
+__global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int BH, int N, int Np, float scale, float scale_log2) {
+  using G = Geo<D>;
+  constexpr int kDC = G::kDC, kDB = G::kDB;
+  // Two stages of Q, dO, LSE and Delta tiles, each its own array so that
+  // every copy names its target at compile time.
+  __shared__ __attribute__((aligned(1024))) char qs0[G::kBytes];
+  __shared__ __attribute__((aligned(1024))) char qs1[G::kBytes];
+  __shared__ __attribute__((aligned(1024))) char gs0[G::kBytes];
+  __shared__ __attribute__((aligned(1024))) char gs1[G::kBytes];
+  __shared__ __attribute__((aligned(256))) float ls0[kTile];
+  __shared__ __attribute__((aligned(256))) float ls1[kTile];
+  __shared__ __attribute__((aligned(256))) float es0[kTile];
+  __shared__ __attribute__((aligned(256))) float es1[kTile];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int nkb = (N + kBlk - 1) / kBlk;
+  int bh, kb;
+  block_of(blockIdx.x, nkb, BH, bh, kb);  // causal: the heaviest blocks (kb = 0) first
+  const int64_t head = (int64_t)bh * N * D;
+  const int head_bytes = N * D * 2;
+  const int kw = kb * kBlk + wave * 32;  // first key of this wave
+  const int key = kw + col;              // this lane's key
+
+  // B operands of S = Q K^T and dP = dO V^T: key `key`, dims 16 c + 8 half + 0..7.
+  bf16x8 kreg[kDC], vreg[kDC];
+#pragma unroll
+  for (int c = 0; c < kDC; ++c) {
+    const int64_t e = head + (int64_t)key * D + c * 16 + half * 8;
+    kreg[c] = key < N ? *reinterpret_cast<const bf16x8*>(k + e) : bf16x8{};
+    vreg[c] = key < N ? *reinterpret_cast<const bf16x8*>(v + e) : bf16x8{};
+  }
+  f32x16 dka[kDB], dva[kDB];
+#pragma unroll
+  for (int b = 0; b < kDB; ++b) dka[b] = dva[b] = f32x16{};
+
+  int coff[G::kCopies];
+#pragma unroll
+  for (int i = 0; i < G::kCopies; ++i) {
+    const int p = (wave * G::kCopies + i) * 64 + lane;
+    const int r = p / G::kUnits, u = p % G::kUnits;
+    coff[i] = r * G::kRow + ((u ^ G::swz(r)) << 4);
+  }
+  const ReadOffsets<D> off = read_offsets<D>(lane);
+  const float* lse2_h = lse2 + (int64_t)bh * Np;
+  const float* delta_h = delta + (int64_t)bh * Np;
+
+  const int nqt = (N + kTile - 1) / kTile;
+  // Causal: query rows below the block's first key see none of its keys.
+  const int t_begin = kCausal ? kb * (kBlk / kTile) : 0;
+  if (t_begin >= nqt) return;  // uniform over the workgroup; cannot happen for kb < nkb
+
+  auto issue = [&](char* qb, char* gb, float* lb, float* eb, int t) __attribute__((always_inline)) {
+    const int row0 = t * kTile;
+    copy_rows<D>(qb, q + head, head_bytes, row0, wave, coff);
+    copy_rows<D>(gb, dout + head, head_bytes, row0, wave, coff);
+    if (wave == 0) copy_vec64(lb, lse2_h + row0, lane);
+    if (wave == 1) copy_vec64(eb, delta_h + row0, lane);
+  };
+
+  // One 64-row tile: two 32-row sub-tiles.
+  auto compute = [&](auto masked, const char* qb, const char* gb, const float* lb,
+                     const float* eb, int t) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int r0 = s * 32;
+      const int qbase = t * kTile + r0;  // first query row of the sub-tile
+      // Causal: every query row of the sub-tile is before this wave's keys.
+      if (kMasked && kw > qbase + 31) continue;
+      f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int c = 0; c < kDC; ++c) {
+        sc = mfma32(read_row<D>(qb, off, c, r0), kreg[c], sc);
+        dp = mfma32(read_row<D>(gb, off, c, r0), vreg[c], dp);
+      }
+      // Row statistics of rows r0 + 8 j + 4 half + 0..3.
+      f32x4 l4[4], e4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l4[j] = *reinterpret_cast<const f32x4*>(lb + r0 + 8 * j + 4 * half);
+        e4[j] = *reinterpret_cast<const f32x4*>(eb + r0 + 8 * j + 4 * half);
+      }
+      // Key `key` is visible from row qbase + 4 half + rho when rho >= lim.
+      const int lim = key - qbase - 4 * half;
+      float p[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -l4[i >> 2][i & 3]));
+        if (kMasked && rho(i) < lim) x = 0.0f;
+        p[i] = x;
+        ds[i] = x * (dp[i] - e4[i >> 2][i & 3]);
+      }
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const bf16x8 pb = pack8(p, kc2);
+        const bf16x8 db = pack8(ds, kc2);
+#pragma unroll
+        for (int b = 0; b < kDB; ++b) {
+          dva[b] = mfma32(read_tr<D>(gb, off, b, r0 + 16 * kc2), pb, dva[b]);
+          dka[b] = mfma32(read_tr<D>(qb, off, b, r0 + 16 * kc2), db, dka[b]);
+        }
+      }
+    }
+  };
+  using Masked = std::integral_constant<bool, true>;
+  using Plain = std::integral_constant<bool, false>;
+  // Causal: the first two tiles of the block cross the diagonal.
+  auto run = [&](const char* qb, const char* gb, const float* lb, const float* eb, int t) __attribute__((always_inline)) {
+    if (kCausal && t < t_begin + kBlk / kTile) compute(Masked{}, qb, gb, lb, eb, t);
+    else compute(Plain{}, qb, gb, lb, eb, t);
+  };
+
+  issue(qs0, gs0, ls0, es0, t_begin);
+  for (int t = t_begin; t < nqt; t += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < nqt) issue(qs1, gs1, ls1, es1, t + 1);
+    run(qs0, gs0, ls0, es0, t);
+    if (t + 1 >= nqt) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 2 < nqt) issue(qs0, gs0, ls0, es0, t + 2);
+    run(qs1, gs1, ls1, es1, t + 1);
+  }
+
+  // dK^T and dV^T: lane = key, register i of block b = dim 32 b + 8 (i / 4)
+  // + 4 half + i % 4.
+  if (key < N) {
+    uint16_t* dkr = dk + head + (int64_t)key * D;
+    uint16_t* dvr = dv + head + (int64_t)key * D;
+#pragma unroll
+    for (int b = 0; b < kDB; ++b) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = b * 32 + 8 * j + 4 * half;
+        store4(dkr + d, dka[b], 4 * j, scale);
+        store4(dvr + d, dva[b], 4 * j, 1.0f);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq: dQ of 128 query rows per workgroup.
+// ---------------------------------------------------------------------------
+template <int D, bool kCausal>
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dq,
+    int BH, int N, int Np, float scale, float scale_log2) {
+  using G = Geo<D>;
+  constexpr int kDC = G::kDC, kDB = G::kDB;
+  __shared__ __attribute__((aligned(1024))) char ks0[G::kBytes];
+  __shared__ __attribute__((aligned(1024))) char ks1[G::kBytes];
+  __shared__ __attribute__((aligned(1024))) char vs0[G::kBytes];
+  __shared__ __attribute__((aligned(1024))) char vs1[G::kBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int nqb = (N + kBlk - 1) / kBlk;
+  int bh, rank;
+  block_of(blockIdx.x, nqb, BH, bh, rank);
+  const int qt = kCausal ? nqb - 1 - rank : rank;  // causal: the heaviest blocks first
+  const int64_t head = (int64_t)bh * N * D;
+  const int head_bytes = N * D * 2;
+  const int qw = qt * kBlk + wave * 32;  // first query row of this wave
+  const int qrow = qw + col;             // this lane's query row (< Np)
+
+  // B operands of S^T = K Q^T and dP^T = V dO^T: row `qrow`, dims
+  // 16 c + 8 half + 0..7.
+  bf16x8 qreg[kDC], oreg[kDC];
+#pragma unroll
+  for (int c = 0; c < kDC; ++c) {
+    const int64_t e = head + (int64_t)qrow * D + c * 16 + half * 8;
+    qreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(q + e) : bf16x8{};
+    oreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(dout + e) : bf16x8{};
+  }
+  const float l2 = lse2[(int64_t)bh * Np + qrow];
+  const float dl = delta[(int64_t)bh * Np + qrow];
+  f32x16 dqa[kDB];
+#pragma unroll
+  for (int b = 0; b < kDB; ++b) dqa[b] = f32x16{};
+
+  int coff[G::kCopies];
+#pragma unroll
+  for (int i = 0; i < G::kCopies; ++i) {
+    const int p = (wave * G::kCopies + i) * 64 + lane;
+    const int r = p / G::kUnits, u = p % G::kUnits;
+    coff[i] = r * G::kRow + ((u ^ G::swz(r)) << 4);
+  }
+  const ReadOffsets<D> off = read_offsets<D>(lane);
+
+  const int nkt = (N + kTile - 1) / kTile;
+  // Causal: keys past the block's last query row are hidden from all of it.
+  const int t_end = kCausal ? min(nkt, (qt + 1) * (kBlk / kTile)) : nkt;
+  // The last key visible from this lane's row, plus one.
+  const int vis_end = kCausal ? min(qrow + 1, N) : N;
+
+  auto issue = [&](char* kbuf, char* vbuf, int t) __attribute__((always_inline)) {
+    copy_rows<D>(kbuf, k + head, head_bytes, t * kTile, wave, coff);
+    copy_rows<D>(vbuf, v + head, head_bytes, t * kTile, wave, coff);
+  };
+
+  auto compute = [&](auto masked, const char* kbuf, const char* vbuf, int t) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int r0 = s * 32;
+      const int kbase = t * kTile + r0;  // first key of the sub-tile
+      // Masked tiles: every key of the sub-tile is hidden from this wave.
+      if (kMasked && (kbase >= N || (kCausal && kbase > qw + 31))) continue;
+      f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int c = 0; c < kDC; ++c) {
+        sc = mfma32(read_row<D>(kbuf, off, c, r0), qreg[c], sc);
+        dp = mfma32(read_row<D>(vbuf, off, c, r0), oreg[c], dp);
+      }
+      // Key kbase + 4 half + rho is visible from this row when rho < lim.
+      const int lim = vis_end - kbase - 4 * half;
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -l2));
+        if (kMasked && rho(i) >= lim) x = 0.0f;
+        ds[i] = x * (dp[i] - dl);
+      }
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const bf16x8 db = pack8(ds, kc2);
+#pragma unroll
+        for (int b = 0; b < kDB; ++b)
+          dqa[b] = mfma32(read_tr<D>(kbuf, off, b, r0 + 16 * kc2), db, dqa[b]);
+      }
+    }
+  };
+  using Masked = std::integral_constant<bool, true>;
+  using Plain = std::integral_constant<bool, false>;
+  // Masked tiles: those crossing the causal diagonal or the end of the keys.
+  const int t_plain_end = min(kCausal ? qt * (kBlk / kTile) : nkt, N / kTile);
+  auto run = [&](const char* kbuf, const char* vbuf, int t) __attribute__((always_inline)) {
+    if (t >= t_plain_end) compute(Masked{}, kbuf, vbuf, t);
+    else compute(Plain{}, kbuf, vbuf, t);
+  };
+
+  issue(ks0, vs0, 0);
+  for (int t = 0; t < t_end; t += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < t_end) issue(ks1, vs1, t + 1);
+    run(ks0, vs0, t);
+    if (t + 1 >= t_end) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 2 < t_end) issue(ks0, vs0, t + 2);
+    run(ks1, vs1, t + 1);
+  }
+
+  // dQ^T: lane = query row, register i of block b = dim 32 b + 8 (i / 4) +
+  // 4 half + i % 4.
+  if (qrow < N) {
+    uint16_t* dqr = dq + head + (int64_t)qrow * D;
+#pragma unroll
+    for (int b = 0; b < kDB; ++b) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store4(dqr + b * 32 + 8 * j + 4 * half, dqa[b], 4 * j, scale);
+    }
+  }
+}
+
+template <int D, bool kCausal>
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, int BH, int N, float scale,
+                      void* workspace, hipStream_t stream) {
+  const int Np = (N + kPad - 1) / kPad * kPad;
+  float* delta = static_cast<float*>(workspace);
+  float* lse2 = delta + (int64_t)BH * Np;
+  const float scale_log2 = scale * kLog2e;
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* k16 = static_cast<const uint16_t*>(k);
+  const auto* v16 = static_cast<const uint16_t*>(v);
+  const auto* g16 = static_cast<const uint16_t*>(dout);
+  const int64_t prep_threads = (int64_t)BH * Np * (D / 8);
+  attn_bwd_prep_kernel<D><<<dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, stream>>>(
+      static_cast<const uint16_t*>(o), g16, lse, delta, lse2, BH, N, Np);
+  const unsigned blocks = (unsigned)((int64_t)BH * ((N + kBlk - 1) / kBlk));
+  attn_bwd_dkdv_kernel<D, kCausal><<<dim3(blocks), dim3(kThreads), 0, stream>>>(
+      q16, k16, v16, g16, lse2, delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), BH,
+      N, Np, scale, scale_log2);
+  attn_bwd_dq_kernel<D, kCausal><<<dim3(blocks), dim3(kThreads), 0, stream>>>(
+      q16, k16, v16, g16, lse2, delta, static_cast<uint16_t*>(dq), BH, N, Np, scale, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t attn_bwd_workspace(int B, int H, int N) {
+  const int64_t Np = ((int64_t)N + kPad - 1) / kPad * kPad;
+  return 2 * 4 * (int64_t)B * H * Np;
+}
+
+hipError_t attn_bwd_launch(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                           int H, int N, int D, float scale, bool causal, void* workspace,
+                           hipStream_t stream) {
+  const int BH = B * H;
+  if (D == 128) {
+    return causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, N, scale,
+                                          workspace, stream)
+                  : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, N, scale,
+                                           workspace, stream);
+  }
+  return causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, N, scale, workspace,
+                                       stream)
+                : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, N, scale,
+                                        workspace, stream);
+}
+
+}  // namespace osm

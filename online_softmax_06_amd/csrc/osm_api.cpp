@@ -163,6 +163,28 @@ int osm_attn_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                                              workspace, static_cast<hipStream_t>(stream)));
 }
 
+int64_t osm_attn_bwd_workspace(int B, int H, int N, int D) {
+  if (B < 0 || H < 0 || N < 0) return -1;
+  if (D != 64 && D != 128) return -1;
+  if ((int64_t)B * H > INT32_MAX) return -1;
+  return osm::attn_bwd_workspace(B, H, N);  // < 8 * 2^31 * 2^31: no overflow
+}
+
+int osm_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int D,
+                 float scale, int causal, void* workspace, int64_t workspace_bytes, void* stream) {
+  const int st = check_attn(q, k, v, o, lse, B, H, N, D, scale, nullptr, nullptr, 0, 0, 1);
+  if (st != OSM_OK || (int64_t)B * H * N == 0) return st;
+  if (!dout || !dq || !dk || !dv) return OSM_ERR_INVALID_ARG;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return OSM_ERR_INVALID_ARG;
+  const int64_t need = osm_attn_bwd_workspace(B, H, N, D);
+  if (need < 0 || workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+    return OSM_ERR_INVALID_ARG;
+  return from_hip(osm::attn_bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
+                                       causal != 0, workspace, static_cast<hipStream_t>(stream)));
+}
+
 int osm_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int D, float scale, int causal, void* stream) {
   return osm_attn_fwd_ex(q, k, v, o, lse, B, H, N, D, scale, causal, nullptr, nullptr, 0, 0,

@@ -55,7 +55,8 @@ def attention_probs_head_ref(q, k, scale, causal, kv_len=None, bias=None):
     return P
 
 
-def attention_bwd_head_ref(q, k, v, do, scale, causal, kv_len=None, bias=None):
+def attention_bwd_head_ref(q, k, v, do, scale, causal, kv_len=None, bias=None,
+                           return_probs=False):
     """Gradients of one (batch, head) slice, float64.
 
     With P from ``attention_probs_head_ref`` and c the float32 scale widened:
@@ -65,7 +66,8 @@ def attention_bwd_head_ref(q, k, v, do, scale, causal, kv_len=None, bias=None):
         dQ = c dS K,   dK = c dS^T Q.
     Masked entries have P = 0 and therefore dS = 0.
 
-    Returns (dQ, dK, dV) as float64 arrays shaped like q, k, v.
+    Returns (dQ, dK, dV) as float64 arrays shaped like q, k, v; with
+    ``return_probs`` also P and dS (Nq x Nk).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -78,6 +80,8 @@ def attention_bwd_head_ref(q, k, v, do, scale, causal, kv_len=None, bias=None):
     dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
     dQ = c * (dS @ k)
     dK = c * (dS.T @ q)
+    if return_probs:
+        return dQ, dK, dV, P, dS
     return dQ, dK, dV
 
 

@@ -31,7 +31,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split",
+    assert _declared_functions() == ["osm_attn_bwd", "osm_attn_bwd_workspace",
+                                     "osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split",
                                      "osm_attn_fwd_split_workspace", "osm_softmax_rows",
                                      "osm_softmax_rows_ex", "osm_softmax_rows_split",
                                      "osm_softmax_rows_split_workspace", "osm_status_string",
@@ -172,3 +173,33 @@ def test_attn_split_workspace_size(lib):
 def test_attn_split_argument_checks(lib, splits, ws, wsb, expect):
     assert osm.osm_attn_fwd_split(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 300, 128, 0.1, 1, 0, 0, 0, 0,
                                   splits, ws, wsb, 0) == expect
+
+
+def test_attn_bwd_workspace_size(lib):
+    assert osm.osm_attn_bwd_workspace(2, 3, 100, 128) == 8 * 6 * 128
+    assert osm.osm_attn_bwd_workspace(1, 1, 129, 64) == 8 * 256
+    assert osm.osm_attn_bwd_workspace(1, 1, 0, 64) == 0
+    assert osm.osm_attn_bwd_workspace(1, 1, 10, 96) == -1
+    assert osm.osm_attn_bwd_workspace(-1, 1, 10, 64) == -1
+
+
+def _bwd(B=1, H=2, N=300, D=128, scale=0.1, causal=1, ptrs=None, ws=FAKE, wsb=1 << 30):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    return osm.osm_attn_bwd(*p, B, H, N, D, scale, causal, ws, wsb, 0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(D=96), osm.OSM_ERR_UNSUPPORTED),
+    (dict(N=-1), osm.OSM_ERR_INVALID_ARG),
+    (dict(scale=0.0), osm.OSM_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), osm.OSM_ERR_INVALID_ARG),
+    (dict(ws=0), osm.OSM_ERR_INVALID_ARG),
+    (dict(wsb=8 * 2 * 384 - 1), osm.OSM_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 4), osm.OSM_ERR_INVALID_ARG),
+    (dict(ptrs=[FAKE] * 5 + [0] + [FAKE] * 3), osm.OSM_ERR_INVALID_ARG),   # no dout
+    (dict(ptrs=[FAKE] * 6 + [FAKE + 2] + [FAKE] * 2), osm.OSM_ERR_INVALID_ARG),  # dq misaligned
+    (dict(ptrs=[FAKE] * 8 + [0]), osm.OSM_ERR_INVALID_ARG),   # no dv
+    (dict(N=0, ptrs=[0] * 9, ws=0, wsb=0), osm.OSM_OK),        # empty: nothing to do
+])
+def test_attn_bwd_argument_checks(lib, kw, expect):
+    assert _bwd(**kw) == expect
