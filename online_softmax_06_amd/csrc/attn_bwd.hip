@@ -131,6 +131,7 @@ template <int D>
 struct ReadOffsets {
   int row;
   int tr[D / 32];
+  int trx[D / 32];  // tr[b] ^ kPartXor: the same read 8 rows further down
 };
 
 template <int D>
@@ -146,6 +147,7 @@ __device__ __forceinline__ ReadOffsets<D> read_offsets(int lane) {
   for (int b = 0; b < G::kDB; ++b) {
     const int d = b * 32 + td;
     o.tr[b] = trow * G::kRow + (((d >> 3) ^ G::swz(trow)) << 4) + (d & 7) * 2;
+    o.trx[b] = o.tr[b] ^ G::kPartXor;
   }
   return o;
 }
@@ -158,8 +160,10 @@ template <int D>
 __device__ __forceinline__ bf16x8 read_tr(const char* tile, const ReadOffsets<D>& off, int b,
                                           int r0) {
   using G = Geo<D>;
+  // Adding whole rows leaves the bits of kPartXor alone, so both offsets are
+  // a per-lane register plus a constant.
   const int o0 = off.tr[b] + r0 * G::kRow;
-  const int o1 = (o0 + 8 * G::kRow) ^ G::kPartXor;
+  const int o1 = off.trx[b] + (r0 + 8) * G::kRow;
   const s16x4 v0 =
       __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + o0));
   const s16x4 v1 =
@@ -185,6 +189,62 @@ __device__ __forceinline__ bf16x8 pack8(const float (&x)[16], int kc2) {
 
 // Output register i of a 32 x 32 product sits in row rho(i) + 4 half.
 __device__ __forceinline__ constexpr int rho(int i) { return (i >> 2) * 8 + (i & 3); }
+
+// The two first products of a 32-row sub-tile, s1 = A1 B1 and s2 = A2 B2
+// over the kDC slices of the head dimension: A rows [r0, r0 + 32) of the
+// streamed tiles t1 and t2, B in registers.  Each region (fenced by
+// sched_barrier) issues one product of each and the LDS reads of the next
+// slice, so few operands are live at a time.
+template <int D>
+__device__ __forceinline__ void first_products(const char* t1, const char* t2,
+                                               const ReadOffsets<D>& off, int r0,
+                                               const bf16x8 (&b1)[D / 16],
+                                               const bf16x8 (&b2)[D / 16], f32x16& s1,
+                                               f32x16& s2) {
+  constexpr int kDC = D / 16;
+  bf16x8 a1[2], a2[2];
+  a1[0] = read_row<D>(t1, off, 0, r0);
+  a2[0] = read_row<D>(t2, off, 0, r0);
+  s1 = f32x16{};
+  s2 = f32x16{};
+#pragma unroll
+  for (int c = 0; c < kDC; ++c) {
+    if (c + 1 < kDC) {
+      a1[(c + 1) & 1] = read_row<D>(t1, off, c + 1, r0);
+      a2[(c + 1) & 1] = read_row<D>(t2, off, c + 1, r0);
+    }
+    s1 = mfma32(a1[c & 1], b1[c], s1);
+    s2 = mfma32(a2[c & 1], b2[c], s2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The accumulating products of a 32-row sub-tile: for each 16-row slice kc2
+// and dim block b, acc1[b] += T1^T B1[kc2] (and acc2[b] += T2^T B2[kc2] when
+// kTwo), the A operands read transposed from the streamed tiles one step
+// ahead, in fenced regions.
+template <int D, bool kTwo>
+__device__ __forceinline__ void acc_products(const char* t1, const char* t2,
+                                             const ReadOffsets<D>& off, int r0,
+                                             const bf16x8 (&b1)[2], const bf16x8 (&b2)[2],
+                                             f32x16 (&acc1)[D / 32], f32x16 (&acc2)[D / 32]) {
+  constexpr int kDB = D / 32, kSteps = 2 * kDB;
+  bf16x8 x1[2], x2[2];
+  x1[0] = read_tr<D>(t1, off, 0, r0);
+  if constexpr (kTwo) x2[0] = read_tr<D>(t2, off, 0, r0);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int kc2 = i / kDB, b = i % kDB;
+    if (i + 1 < kSteps) {
+      const int rn = r0 + 16 * ((i + 1) / kDB), bn = (i + 1) % kDB;
+      x1[(i + 1) & 1] = read_tr<D>(t1, off, bn, rn);
+      if constexpr (kTwo) x2[(i + 1) & 1] = read_tr<D>(t2, off, bn, rn);
+    }
+    acc1[b] = mfma32(x1[i & 1], b1[kc2], acc1[b]);
+    if constexpr (kTwo) acc2[b] = mfma32(x2[i & 1], b2[kc2], acc2[b]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
 // Map a linear workgroup id to (batch*head, block).  Workgroups go
 // round-robin over the 8 XCDs; when B*H is a multiple of 8, all blocks of one
@@ -324,61 +384,68 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
       const int qbase = t * kTile + r0;  // first query row of the sub-tile
       // Causal: every query row of the sub-tile is before this wave's keys.
       if (kMasked && kw > qbase + 31) continue;
-      f32x16 sc = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int c = 0; c < kDC; ++c) {
-        sc = mfma32(read_row<D>(qb, off, c, r0), kreg[c], sc);
-        dp = mfma32(read_row<D>(gb, off, c, r0), vreg[c], dp);
-      }
-      // Row statistics of rows r0 + 8 j + 4 half + 0..3.
-      f32x4 l4[4], e4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        l4[j] = *reinterpret_cast<const f32x4*>(lb + r0 + 8 * j + 4 * half);
-        e4[j] = *reinterpret_cast<const f32x4*>(eb + r0 + 8 * j + 4 * half);
-      }
+      f32x16 sc, dp;
+      first_products<D>(qb, gb, off, r0, kreg, vreg, sc, dp);
       // Key `key` is visible from row qbase + 4 half + rho when rho >= lim.
       const int lim = key - qbase - 4 * half;
+      // P (into sc) and dS (into dp), four rows at a time: rows r0 + 8 j +
+      // 4 half + 0..3, whose LSE and Delta are one 16-byte read each.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + r0 + 8 * j + 4 * half);
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(eb + r0 + 8 * j + 4 * half);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * j + r;
+          float x = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -l4[r]));
+          if (kMasked && rho(i) < lim) x = 0.0f;
+          sc[i] = x;
+          dp[i] = x * (dp[i] - e4[r]);
+        }
+      }
       float p[16], ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float x = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -l4[i >> 2][i & 3]));
-        if (kMasked && rho(i) < lim) x = 0.0f;
-        p[i] = x;
-        ds[i] = x * (dp[i] - e4[i >> 2][i & 3]);
+        p[i] = sc[i];
+        ds[i] = dp[i];
       }
-#pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2) {
-        const bf16x8 pb = pack8(p, kc2);
-        const bf16x8 db = pack8(ds, kc2);
-#pragma unroll
-        for (int b = 0; b < kDB; ++b) {
-          dva[b] = mfma32(read_tr<D>(gb, off, b, r0 + 16 * kc2), pb, dva[b]);
-          dka[b] = mfma32(read_tr<D>(qb, off, b, r0 + 16 * kc2), db, dka[b]);
-        }
-      }
+      const bf16x8 pb[2] = {pack8(p, 0), pack8(p, 1)};
+      const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
+      __builtin_amdgcn_sched_barrier(0);
+      acc_products<D, true>(gb, qb, off, r0, pb, db, dva, dka);
     }
   };
   using Masked = std::integral_constant<bool, true>;
   using Plain = std::integral_constant<bool, false>;
-  // Causal: the first two tiles of the block cross the diagonal.
-  auto run = [&](const char* qb, const char* gb, const float* lb, const float* eb, int t) __attribute__((always_inline)) {
-    if (kCausal && t < t_begin + kBlk / kTile) compute(Masked{}, qb, gb, lb, eb, t);
-    else compute(Plain{}, qb, gb, lb, eb, t);
+  using Stage0 = std::integral_constant<int, 0>;
+  using Stage1 = std::integral_constant<int, 1>;
+  // Tile t sits in stage (t - t_begin) & 1.  A step waits for its tile,
+  // starts the copy of the next one into the other stage and computes.
+  auto step = [&](auto masked, auto stage, int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if constexpr (decltype(stage)::value == 0) {
+      if (t + 1 < nqt) issue(qs1, gs1, ls1, es1, t + 1);
+      compute(masked, qs0, gs0, ls0, es0, t);
+    } else {
+      if (t + 1 < nqt) issue(qs0, gs0, ls0, es0, t + 1);
+      compute(masked, qs1, gs1, ls1, es1, t);
+    }
   };
 
   issue(qs0, gs0, ls0, es0, t_begin);
-  for (int t = t_begin; t < nqt; t += 2) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 1 < nqt) issue(qs1, gs1, ls1, es1, t + 1);
-    run(qs0, gs0, ls0, es0, t);
-    if (t + 1 >= nqt) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 2 < nqt) issue(qs0, gs0, ls0, es0, t + 2);
-    run(qs1, gs1, ls1, es1, t + 1);
+  int t = t_begin;
+  if constexpr (kCausal) {
+    // The first two tiles of the block cross the diagonal.
+    step(Masked{}, Stage0{}, t);
+    if (t + 1 < nqt) step(Masked{}, Stage1{}, t + 1);
+    t += 2;
   }
+  for (; t + 1 < nqt; t += 2) {
+    step(Plain{}, Stage0{}, t);
+    step(Plain{}, Stage1{}, t + 1);
+  }
+  if (t < nqt) step(Plain{}, Stage0{}, t);
 
   // dK^T and dV^T: lane = key, register i of block b = dim 32 b + 8 (i / 4)
   // + 4 half + i % 4.
@@ -468,12 +535,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       const int kbase = t * kTile + r0;  // first key of the sub-tile
       // Masked tiles: every key of the sub-tile is hidden from this wave.
       if (kMasked && (kbase >= N || (kCausal && kbase > qw + 31))) continue;
-      f32x16 sc = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int c = 0; c < kDC; ++c) {
-        sc = mfma32(read_row<D>(kbuf, off, c, r0), qreg[c], sc);
-        dp = mfma32(read_row<D>(vbuf, off, c, r0), oreg[c], dp);
-      }
+      f32x16 sc, dp;
+      first_products<D>(kbuf, vbuf, off, r0, qreg, oreg, sc, dp);
       // Key kbase + 4 half + rho is visible from this row when rho < lim.
       const int lim = vis_end - kbase - 4 * half;
       float ds[16];
@@ -483,13 +546,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
         if (kMasked && rho(i) >= lim) x = 0.0f;
         ds[i] = x * (dp[i] - dl);
       }
-#pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2) {
-        const bf16x8 db = pack8(ds, kc2);
-#pragma unroll
-        for (int b = 0; b < kDB; ++b)
-          dqa[b] = mfma32(read_tr<D>(kbuf, off, b, r0 + 16 * kc2), db, dqa[b]);
-      }
+      const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
+      __builtin_amdgcn_sched_barrier(0);
+      acc_products<D, false>(kbuf, kbuf, off, r0, db, db, dqa, dqa);
     }
   };
   using Masked = std::integral_constant<bool, true>;
