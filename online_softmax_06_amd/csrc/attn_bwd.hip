@@ -76,7 +76,6 @@ struct Geo {
   static constexpr int kBytes = kTile * kRow;
   static constexpr int kDC = D / 16;       // 16-wide slices of the head dimension
   static constexpr int kDB = D / 32;       // 32-wide blocks of the head dimension
-  static constexpr int kCopies = kTile * kUnits / 64 / kWaves;  // 16-byte copies per lane
   // Unit u of row r sits at unit u ^ swz(r).
   //  * Row reads: 16 lanes read one unit of 16 consecutive rows; swz takes 16
   //    distinct values on them (D = 128: 16 units per 256-byte row) or 8
@@ -93,29 +92,42 @@ struct Geo {
   static constexpr int kPartXor = D == 128 ? 16 : 32;
 };
 
-// Global->LDS copy of rows [row0, row0 + kTile) of one head (row-major,
+// Global->LDS copy of rows [row0, row0 + kRows) of one head (row-major,
 // D bfloat16 per row) into `lds`, swizzled: copy i of wave w fills LDS bytes
-// [(w * kCopies + i) * 1024, +1024), one 16-byte unit per lane at the per-lane
-// source offset `off[i]`.  The buffer descriptor starts at row0 and ends with
-// the head, so rows past the head arrive as zeros.
-template <int D>
-__device__ __forceinline__ void copy_rows(char* lds, const uint16_t* head, int head_bytes,
-                                          int row0, int wave, const int (&off)[Geo<D>::kCopies]) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const int left = head_bytes - row0 * Geo<D>::kRow;
-  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(head + (int64_t)row0 * D), 0,
-                                                      left > 0 ? left : 0, kBufferFlags);
+// [(w * kPerWave + i) * 1024, +1024), one 16-byte unit per lane at the
+// per-lane source offset off[i].  The buffer descriptor starts at row0 and
+// ends with the head, so rows past the head arrive as zeros.
+template <int D, int kRows>
+struct RowCopy {
+  static constexpr int kPerWave = kRows * (D / 8) / 64 / kWaves;
+  static_assert(kPerWave >= 1, "every wave issues at least one copy");
+  __device__ static void offsets(int wave, int lane, int (&off)[kPerWave]) {
 #pragma unroll
-  for (int i = 0; i < Geo<D>::kCopies; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, OSM_LDS(lds + (wave * Geo<D>::kCopies + i) * 1024),
-                                             16, off[i], 0, 0, 0);
-#endif
-}
-
-// Global->LDS copy of 64 floats (one per lane) starting at `src`.
-__device__ __forceinline__ void copy_vec64(float* lds, const float* src, int lane) {
+    for (int i = 0; i < kPerWave; ++i) {
+      const int p = (wave * kPerWave + i) * 64 + lane;  // physical unit in the block
+      const int r = p / (D / 8), u = p % (D / 8);
+      off[i] = r * (D * 2) + ((u ^ Geo<D>::swz(r)) << 4);
+    }
+  }
+  __device__ static void issue(char* lds, const uint16_t* head, int head_bytes, int row0,
+                               int wave, const int (&off)[kPerWave]) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, 64 * 4, kBufferFlags);
+    const int left = head_bytes - row0 * (D * 2);
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(head + (int64_t)row0 * D), 0,
+                                                        left > 0 ? left : 0, kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, OSM_LDS(lds + (wave * kPerWave + i) * 1024),
+                                               16, off[i], 0, 0, 0);
+#endif
+  }
+};
+
+// Global->LDS copy of n <= 64 floats starting at `src` into lds[0, 64): lane i
+// copies element i; lanes at or past n store zeros (outside the descriptor).
+__device__ __forceinline__ void copy_vec(float* lds, const float* src, int n, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, n * 4, kBufferFlags);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, OSM_LDS(lds), 4, lane * 4, 0, 0, 0);
 #endif
 }
@@ -195,26 +207,29 @@ __device__ __forceinline__ constexpr int rho(int i) { return (i >> 2) * 8 + (i &
 // streamed tiles t1 and t2, B in registers.  Each region (fenced by
 // sched_barrier) issues one product of each and the LDS reads of the next
 // slice, so few operands are live at a time.
-template <int D>
+template <int D, int kAhead>
 __device__ __forceinline__ void first_products(const char* t1, const char* t2,
                                                const ReadOffsets<D>& off, int r0,
                                                const bf16x8 (&b1)[D / 16],
                                                const bf16x8 (&b2)[D / 16], f32x16& s1,
                                                f32x16& s2) {
-  constexpr int kDC = D / 16;
-  bf16x8 a1[2], a2[2];
-  a1[0] = read_row<D>(t1, off, 0, r0);
-  a2[0] = read_row<D>(t2, off, 0, r0);
+  constexpr int kDC = D / 16, kBuf = kAhead + 1;
+  bf16x8 a1[kBuf], a2[kBuf];
+#pragma unroll
+  for (int c = 0; c < kAhead; ++c) {
+    a1[c] = read_row<D>(t1, off, c, r0);
+    a2[c] = read_row<D>(t2, off, c, r0);
+  }
   s1 = f32x16{};
   s2 = f32x16{};
 #pragma unroll
   for (int c = 0; c < kDC; ++c) {
-    if (c + 1 < kDC) {
-      a1[(c + 1) & 1] = read_row<D>(t1, off, c + 1, r0);
-      a2[(c + 1) & 1] = read_row<D>(t2, off, c + 1, r0);
+    if (c + kAhead < kDC) {
+      a1[(c + kAhead) % kBuf] = read_row<D>(t1, off, c + kAhead, r0);
+      a2[(c + kAhead) % kBuf] = read_row<D>(t2, off, c + kAhead, r0);
     }
-    s1 = mfma32(a1[c & 1], b1[c], s1);
-    s2 = mfma32(a2[c & 1], b2[c], s2);
+    s1 = mfma32(a1[c % kBuf], b1[c], s1);
+    s2 = mfma32(a2[c % kBuf], b2[c], s2);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -223,25 +238,26 @@ __device__ __forceinline__ void first_products(const char* t1, const char* t2,
 // and dim block b, acc1[b] += T1^T B1[kc2] (and acc2[b] += T2^T B2[kc2] when
 // kTwo), the A operands read transposed from the streamed tiles one step
 // ahead, in fenced regions.
-template <int D, bool kTwo>
+template <int D, bool kTwo, int kAhead>
 __device__ __forceinline__ void acc_products(const char* t1, const char* t2,
                                              const ReadOffsets<D>& off, int r0,
                                              const bf16x8 (&b1)[2], const bf16x8 (&b2)[2],
                                              f32x16 (&acc1)[D / 32], f32x16 (&acc2)[D / 32]) {
-  constexpr int kDB = D / 32, kSteps = 2 * kDB;
-  bf16x8 x1[2], x2[2];
-  x1[0] = read_tr<D>(t1, off, 0, r0);
-  if constexpr (kTwo) x2[0] = read_tr<D>(t2, off, 0, r0);
+  constexpr int kDB = D / 32, kSteps = 2 * kDB, kBuf = kAhead + 1;
+  bf16x8 x1[kBuf], x2[kBuf];
+  auto fetch = [&](int i) __attribute__((always_inline)) {
+    const int rn = r0 + 16 * (i / kDB), bn = i % kDB;
+    x1[i % kBuf] = read_tr<D>(t1, off, bn, rn);
+    if constexpr (kTwo) x2[i % kBuf] = read_tr<D>(t2, off, bn, rn);
+  };
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) fetch(i);
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) {
     const int kc2 = i / kDB, b = i % kDB;
-    if (i + 1 < kSteps) {
-      const int rn = r0 + 16 * ((i + 1) / kDB), bn = (i + 1) % kDB;
-      x1[(i + 1) & 1] = read_tr<D>(t1, off, bn, rn);
-      if constexpr (kTwo) x2[(i + 1) & 1] = read_tr<D>(t2, off, bn, rn);
-    }
-    acc1[b] = mfma32(x1[i & 1], b1[kc2], acc1[b]);
-    if constexpr (kTwo) acc2[b] = mfma32(x2[i & 1], b2[kc2], acc2[b]);
+    if (i + kAhead < kSteps) fetch(i + kAhead);
+    acc1[b] = mfma32(x1[i % kBuf], b1[kc2], acc1[b]);
+    if constexpr (kTwo) acc2[b] = mfma32(x2[i % kBuf], b2[kc2], acc2[b]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -306,26 +322,33 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dkdv: dK and dV of 128 keys per workgroup.
+// dkdv: dK and dV of 128 keys per workgroup (32 per wavefront), two
+// workgroups per CU.  The block's K rows stay in LDS (B operand of the
+// scores, read like a streamed tile), its V fragments in registers, and the
+// query rows stream through LDS 32 at a time, double-buffered.
 // ---------------------------------------------------------------------------
 template <int D, bool kCausal>
-__global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int BH, int N, int Np, float scale, float scale_log2) {
   using G = Geo<D>;
   constexpr int kDC = G::kDC, kDB = G::kDB;
-  // Two stages of Q, dO, LSE and Delta tiles, each its own array so that
-  // every copy names its target at compile time.
-  __shared__ __attribute__((aligned(1024))) char qs0[G::kBytes];
-  __shared__ __attribute__((aligned(1024))) char qs1[G::kBytes];
-  __shared__ __attribute__((aligned(1024))) char gs0[G::kBytes];
-  __shared__ __attribute__((aligned(1024))) char gs1[G::kBytes];
-  __shared__ __attribute__((aligned(256))) float ls0[kTile];
-  __shared__ __attribute__((aligned(256))) float ls1[kTile];
-  __shared__ __attribute__((aligned(256))) float es0[kTile];
-  __shared__ __attribute__((aligned(256))) float es1[kTile];
+  constexpr int kSub = 32;  // query rows per streamed tile
+  using KCopy = RowCopy<D, kBlk>;
+  using QCopy = RowCopy<D, kSub>;
+  // K of the block, and two stages of Q, dO, LSE and Delta tiles, each its
+  // own array so that every copy names its target at compile time.
+  __shared__ __attribute__((aligned(1024))) char ks[kBlk * G::kRow];
+  __shared__ __attribute__((aligned(1024))) char qs0[kSub * G::kRow];
+  __shared__ __attribute__((aligned(1024))) char qs1[kSub * G::kRow];
+  __shared__ __attribute__((aligned(1024))) char gs0[kSub * G::kRow];
+  __shared__ __attribute__((aligned(1024))) char gs1[kSub * G::kRow];
+  __shared__ __attribute__((aligned(256))) float ls0[64];
+  __shared__ __attribute__((aligned(256))) float ls1[64];
+  __shared__ __attribute__((aligned(256))) float es0[64];
+  __shared__ __attribute__((aligned(256))) float es1[64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -338,83 +361,97 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   const int kw = kb * kBlk + wave * 32;  // first key of this wave
   const int key = kw + col;              // this lane's key
 
-  // B operands of S = Q K^T and dP = dO V^T: key `key`, dims 16 c + 8 half + 0..7.
-  bf16x8 kreg[kDC], vreg[kDC];
+  {
+    int koff[KCopy::kPerWave];
+    KCopy::offsets(wave, lane, koff);
+    KCopy::issue(ks, k + head, head_bytes, kb * kBlk, wave, koff);
+  }
+  // B operand of dP = dO V^T: key `key`, dims 16 c + 8 half + 0..7.
+  bf16x8 vreg[kDC];
 #pragma unroll
   for (int c = 0; c < kDC; ++c) {
     const int64_t e = head + (int64_t)key * D + c * 16 + half * 8;
-    kreg[c] = key < N ? *reinterpret_cast<const bf16x8*>(k + e) : bf16x8{};
     vreg[c] = key < N ? *reinterpret_cast<const bf16x8*>(v + e) : bf16x8{};
   }
   f32x16 dka[kDB], dva[kDB];
 #pragma unroll
   for (int b = 0; b < kDB; ++b) dka[b] = dva[b] = f32x16{};
 
-  int coff[G::kCopies];
-#pragma unroll
-  for (int i = 0; i < G::kCopies; ++i) {
-    const int p = (wave * G::kCopies + i) * 64 + lane;
-    const int r = p / G::kUnits, u = p % G::kUnits;
-    coff[i] = r * G::kRow + ((u ^ G::swz(r)) << 4);
-  }
+  int coff[QCopy::kPerWave];
+  QCopy::offsets(wave, lane, coff);
   const ReadOffsets<D> off = read_offsets<D>(lane);
   const float* lse2_h = lse2 + (int64_t)bh * Np;
   const float* delta_h = delta + (int64_t)bh * Np;
+  const char* krows = ks + wave * 32 * G::kRow;  // this wave's 32 keys
 
-  const int nqt = (N + kTile - 1) / kTile;
+  const int nst = (N + kSub - 1) / kSub;
   // Causal: query rows below the block's first key see none of its keys.
-  const int t_begin = kCausal ? kb * (kBlk / kTile) : 0;
-  if (t_begin >= nqt) return;  // uniform over the workgroup; cannot happen for kb < nkb
+  const int t_begin = kCausal ? kb * (kBlk / kSub) : 0;
 
   auto issue = [&](char* qb, char* gb, float* lb, float* eb, int t) __attribute__((always_inline)) {
-    const int row0 = t * kTile;
-    copy_rows<D>(qb, q + head, head_bytes, row0, wave, coff);
-    copy_rows<D>(gb, dout + head, head_bytes, row0, wave, coff);
-    if (wave == 0) copy_vec64(lb, lse2_h + row0, lane);
-    if (wave == 1) copy_vec64(eb, delta_h + row0, lane);
+    const int row0 = t * kSub;
+    QCopy::issue(qb, q + head, head_bytes, row0, wave, coff);
+    QCopy::issue(gb, dout + head, head_bytes, row0, wave, coff);
+    if (wave == 0) copy_vec(lb, lse2_h + row0, kSub, lane);
+    if (wave == 1) copy_vec(eb, delta_h + row0, kSub, lane);
   };
 
-  // One 64-row tile: two 32-row sub-tiles.
+  // One 32-row tile: S = Q K^T and dP = dO V^T, P and dS, then
+  // dV^T += dO^T P and dK^T += Q^T dS.
   auto compute = [&](auto masked, const char* qb, const char* gb, const float* lb,
                      const float* eb, int t) __attribute__((always_inline)) {
     constexpr bool kMasked = decltype(masked)::value;
+    const int qbase = t * kSub;  // first query row of the tile
+    // Causal: every query row of the tile is before this wave's keys.
+    if (kMasked && kw > qbase + 31) return;
+    f32x16 sc = f32x16{}, dp = f32x16{};
+    {
+      constexpr int kAhead = 1, kBuf = kAhead + 1;
+      bf16x8 a1[kBuf], a2[kBuf], bk[kBuf];
+      auto fetch = [&](int c) __attribute__((always_inline)) {
+        a1[c % kBuf] = read_row<D>(qb, off, c, 0);
+        bk[c % kBuf] = read_row<D>(krows, off, c, 0);
+        a2[c % kBuf] = read_row<D>(gb, off, c, 0);
+      };
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int r0 = s * 32;
-      const int qbase = t * kTile + r0;  // first query row of the sub-tile
-      // Causal: every query row of the sub-tile is before this wave's keys.
-      if (kMasked && kw > qbase + 31) continue;
-      f32x16 sc, dp;
-      first_products<D>(qb, gb, off, r0, kreg, vreg, sc, dp);
-      // Key `key` is visible from row qbase + 4 half + rho when rho >= lim.
-      const int lim = key - qbase - 4 * half;
-      // P (into sc) and dS (into dp), four rows at a time: rows r0 + 8 j +
-      // 4 half + 0..3, whose LSE and Delta are one 16-byte read each.
+      for (int c = 0; c < kAhead; ++c) fetch(c);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + r0 + 8 * j + 4 * half);
-        const f32x4 e4 = *reinterpret_cast<const f32x4*>(eb + r0 + 8 * j + 4 * half);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * j + r;
-          float x = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -l4[r]));
-          if (kMasked && rho(i) < lim) x = 0.0f;
-          sc[i] = x;
-          dp[i] = x * (dp[i] - e4[r]);
-        }
+      for (int c = 0; c < kDC; ++c) {
+        if (c + kAhead < kDC) fetch(c + kAhead);
+        sc = mfma32(a1[c % kBuf], bk[c % kBuf], sc);
+        dp = mfma32(a2[c % kBuf], vreg[c], dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      float p[16], ds[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = sc[i];
-        ds[i] = dp[i];
-      }
-      const bf16x8 pb[2] = {pack8(p, 0), pack8(p, 1)};
-      const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
-      __builtin_amdgcn_sched_barrier(0);
-      acc_products<D, true>(gb, qb, off, r0, pb, db, dva, dka);
     }
+    // Key `key` is visible from row qbase + 4 half + rho when rho >= lim.
+    const int lim = key - qbase - 4 * half;
+    // P (into sc) and dS (into dp), four rows at a time: rows 8 j + 4 half +
+    // 0..3, whose LSE and Delta are one 16-byte read each.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + 8 * j + 4 * half);
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(eb + 8 * j + 4 * half);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * j + r;
+        float x = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -l4[r]));
+        if (kMasked && rho(i) < lim) x = 0.0f;
+        sc[i] = x;
+        dp[i] = x * (dp[i] - e4[r]);
+      }
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = sc[i];
+      ds[i] = dp[i];
+    }
+    const bf16x8 pb[2] = {pack8(p, 0), pack8(p, 1)};
+    const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
+    __builtin_amdgcn_sched_barrier(0);
+    acc_products<D, true, 1>(gb, qb, off, 0, pb, db, dva, dka);
   };
+
   using Masked = std::integral_constant<bool, true>;
   using Plain = std::integral_constant<bool, false>;
   using Stage0 = std::integral_constant<int, 0>;
@@ -425,10 +462,10 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if constexpr (decltype(stage)::value == 0) {
-      if (t + 1 < nqt) issue(qs1, gs1, ls1, es1, t + 1);
+      if (t + 1 < nst) issue(qs1, gs1, ls1, es1, t + 1);
       compute(masked, qs0, gs0, ls0, es0, t);
     } else {
-      if (t + 1 < nqt) issue(qs0, gs0, ls0, es0, t + 1);
+      if (t + 1 < nst) issue(qs0, gs0, ls0, es0, t + 1);
       compute(masked, qs1, gs1, ls1, es1, t);
     }
   };
@@ -436,16 +473,18 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   issue(qs0, gs0, ls0, es0, t_begin);
   int t = t_begin;
   if constexpr (kCausal) {
-    // The first two tiles of the block cross the diagonal.
+    // The four tiles over the block's own key range cross the diagonal.
     step(Masked{}, Stage0{}, t);
-    if (t + 1 < nqt) step(Masked{}, Stage1{}, t + 1);
-    t += 2;
+    if (t + 1 < nst) step(Masked{}, Stage1{}, t + 1);
+    if (t + 2 < nst) step(Masked{}, Stage0{}, t + 2);
+    if (t + 3 < nst) step(Masked{}, Stage1{}, t + 3);
+    t += 4;
   }
-  for (; t + 1 < nqt; t += 2) {
+  for (; t + 1 < nst; t += 2) {
     step(Plain{}, Stage0{}, t);
     step(Plain{}, Stage1{}, t + 1);
   }
-  if (t < nqt) step(Plain{}, Stage0{}, t);
+  if (t < nst) step(Plain{}, Stage0{}, t);
 
   // dK^T and dV^T: lane = key, register i of block b = dim 32 b + 8 (i / 4)
   // + 4 half + i % 4.
@@ -507,13 +546,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int b = 0; b < kDB; ++b) dqa[b] = f32x16{};
 
-  int coff[G::kCopies];
-#pragma unroll
-  for (int i = 0; i < G::kCopies; ++i) {
-    const int p = (wave * G::kCopies + i) * 64 + lane;
-    const int r = p / G::kUnits, u = p % G::kUnits;
-    coff[i] = r * G::kRow + ((u ^ G::swz(r)) << 4);
-  }
+  using KVCopy = RowCopy<D, kTile>;
+  int coff[KVCopy::kPerWave];
+  KVCopy::offsets(wave, lane, coff);
   const ReadOffsets<D> off = read_offsets<D>(lane);
 
   const int nkt = (N + kTile - 1) / kTile;
@@ -523,8 +558,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   const int vis_end = kCausal ? min(qrow + 1, N) : N;
 
   auto issue = [&](char* kbuf, char* vbuf, int t) __attribute__((always_inline)) {
-    copy_rows<D>(kbuf, k + head, head_bytes, t * kTile, wave, coff);
-    copy_rows<D>(vbuf, v + head, head_bytes, t * kTile, wave, coff);
+    KVCopy::issue(kbuf, k + head, head_bytes, t * kTile, wave, coff);
+    KVCopy::issue(vbuf, v + head, head_bytes, t * kTile, wave, coff);
   };
 
   auto compute = [&](auto masked, const char* kbuf, const char* vbuf, int t) __attribute__((always_inline)) {
@@ -536,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       // Masked tiles: every key of the sub-tile is hidden from this wave.
       if (kMasked && (kbase >= N || (kCausal && kbase > qw + 31))) continue;
       f32x16 sc, dp;
-      first_products<D>(kbuf, vbuf, off, r0, qreg, oreg, sc, dp);
+      first_products<D, 1>(kbuf, vbuf, off, r0, qreg, oreg, sc, dp);
       // Key kbase + 4 half + rho is visible from this row when rho < lim.
       const int lim = vis_end - kbase - 4 * half;
       float ds[16];
@@ -548,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       }
       const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
       __builtin_amdgcn_sched_barrier(0);
-      acc_products<D, false>(kbuf, kbuf, off, r0, db, db, dqa, dqa);
+      acc_products<D, false, 1>(kbuf, kbuf, off, r0, db, db, dqa, dqa);
     }
   };
   using Masked = std::integral_constant<bool, true>;
