@@ -6,6 +6,11 @@ One step is one pass of the whole path over resident synthetic inputs:
   3. fused causal attention forward, bfloat16, B=8 H=40 N=2048 D=128
      (LLaMA-2-13B-shaped layer; bound by the bf16 matrix cores)
 
+Also timed, outside the step (its own loop over the same number of launches):
+  4. attention backward (dQ, dK, dV from the forward's O and LSE) on the same
+     layer, reported under ``attention_backward`` and in ``rooflines`` with
+     ``"in_step": false``.
+
 Printed: one JSON line.  ``value`` is the softmax throughput of the
 bandwidth-scale workload (algorithmic bytes of both softmax runs / their
 kernel time); the attention throughput is in ``attention``.  ``rooflines``
@@ -64,10 +69,10 @@ def read_traffic():
 
 
 class Unit:
-    def __init__(self, name, kernel, src, launch, work, bound, peak, unit, workload):
+    def __init__(self, name, kernel, src, launch, work, bound, peak, unit, workload, in_step=True):
         self.name, self.kernel, self.src = name, kernel, src
         self.launch, self.work, self.bound, self.peak = launch, work, bound, peak
-        self.unit, self.workload = unit, workload
+        self.unit, self.workload, self.in_step = unit, workload, in_step
         self.times_ms = []
 
 
@@ -100,6 +105,25 @@ def make_units(torch, osm, osm_inputs, only):
                                                         cfg["causal"], out=o, lse=lse)),
             flops, "mfma", BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
             f"attn_llama13b B{a['B']} H{a['H']} N{a['N']} D{a['D']} causal"))
+    if only in (None, "attn_bwd"):
+        cfg = osm_inputs.attention_config("attn_llama13b", device="cuda")
+        a = cfg["cfg"]
+        do = osm_inputs.attention_grad_output(a["B"], a["H"], a["N"], a["D"], seed=a["seed"],
+                                              device="cuda")
+        o, lse = osm.attn_fwd(cfg["q"], cfg["k"], cfg["v"], cfg["scale"], cfg["causal"])
+        grads = [torch.empty_like(cfg["q"]) for _ in range(3)]
+        # Algorithmic FLOPs: the five products of the backward (S recomputed,
+        # dP, dV, dK, dQ), 2 * D each per unmasked (query, key) pair.
+        pairs = a["N"] * (a["N"] + 1) // 2 if a["causal"] else a["N"] * a["N"]
+        flops = 10 * a["D"] * pairs * a["B"] * a["H"]
+        units.append(Unit(
+            "attn_bwd", "attn_bwd prep + dkdv + dq kernels <128, causal>", "attn_bwd.hip",
+            (lambda cfg=cfg, o=o, lse=lse, do=do, g=grads: osm.attn_bwd(
+                cfg["q"], cfg["k"], cfg["v"], o, lse, do, scale=cfg["scale"],
+                causal=cfg["causal"], dq=g[0], dk=g[1], dv=g[2])),
+            flops, "mfma", BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
+            f"attn_llama13b B{a['B']} H{a['H']} N{a['N']} D{a['D']} causal, backward",
+            in_step=False))
     return units
 
 
@@ -116,7 +140,7 @@ def cpu_baseline(torch, osm_inputs, budget_s):
     x = osm_inputs.softmax_large(device="cuda")
     rows_done, t_sm = 0, 0.0
     chunk = 1024
-    while rows_done < c["rows"] and t_sm < budget_s * 0.6:
+    while rows_done < c["rows"] and t_sm < budget_s * 0.5:
         xs = x[rows_done:rows_done + chunk].double().cpu().numpy()
         t0 = time.perf_counter()
         softmax_rows_ref(xs)
@@ -129,7 +153,7 @@ def cpu_baseline(torch, osm_inputs, budget_s):
     heads = osm_inputs.sample_heads(a["B"], a["H"], a["B"] * a["H"], a["seed"], [(0, 0)])
     done, t_at = [], 0.0
     for (b, h) in heads:
-        if t_at >= budget_s * 0.4:
+        if t_at >= budget_s * 0.25:
             break
         q, k, v = (cfg[n][b, h][None, None].double().cpu().numpy() for n in ("q", "k", "v"))
         t0 = time.perf_counter()
@@ -137,6 +161,19 @@ def cpu_baseline(torch, osm_inputs, budget_s):
         t_at += time.perf_counter() - t0
         done.append((b, h))
     at_flops = 4 * a["D"] * (a["N"] * (a["N"] + 1) // 2) * len(done)
+    from oracle import attention_bwd_head_ref
+    do = osm_inputs.attention_grad_output(a["B"], a["H"], a["N"], a["D"], seed=a["seed"],
+                                          device="cuda")
+    done_b, t_bw = [], 0.0
+    for (b, h) in heads:
+        if t_bw >= budget_s * 0.25:
+            break
+        q, k, v, g = (t[b, h].double().cpu().numpy() for t in (cfg["q"], cfg["k"], cfg["v"], do))
+        t0 = time.perf_counter()
+        attention_bwd_head_ref(q, k, v, g, cfg["scale"], True)
+        t_bw += time.perf_counter() - t0
+        done_b.append((b, h))
+    bw_flops = 10 * a["D"] * (a["N"] * (a["N"] + 1) // 2) * len(done_b)
     return {
         "value": round(sm_bytes / t_sm / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "sample": (f"float64 three-pass softmax oracle (numpy, single-threaded) on the first "
@@ -146,6 +183,12 @@ def cpu_baseline(torch, osm_inputs, budget_s):
             "cores": blas_threads, "kind": "oracle",
             "sample": (f"float64 materialised-score oracle (numpy + BLAS) on {len(done)} of "
                        f"{a['B'] * a['H']} (b, h) slices of attn_llama13b ({t_at:.1f} s)")},
+        "attention_backward": {
+            "value": round(bw_flops / t_bw / 1e12, 6), "unit": "TFLOP/s",
+            "cores": blas_threads, "kind": "oracle",
+            "sample": (f"float64 softmax-Jacobian gradient oracle (numpy + BLAS) on "
+                       f"{len(done_b)} of {a['B'] * a['H']} (b, h) slices of attn_llama13b "
+                       f"({t_bw:.1f} s); FLOPs counted as the library's five products")},
     }
 
 
@@ -154,7 +197,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["softmax_f32", "softmax_bf16", "attn"], default=None)
+    ap.add_argument("--only", choices=["softmax_f32", "softmax_bf16", "attn", "attn_bwd"],
+                    default=None)
     ap.add_argument("--copy", action="store_true", help="time a plain device copy instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -194,9 +238,11 @@ def main():
                           "GB/s": 2 * x.numel() * 4 / ms / 1e6}))
         return
 
-    units = make_units(torch, osm, osm_inputs, args.only)
+    all_units = make_units(torch, osm, osm_inputs, args.only)
+    units = [u for u in all_units if u.in_step]
+    extra = [u for u in all_units if not u.in_step]
     for _ in range(args.warmup):
-        for u in units:
+        for u in all_units:
             u.launch()
     torch.cuda.synchronize()
 
@@ -214,14 +260,25 @@ def main():
             marks[s][i][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps if units else 0.0
     for s in range(args.steps):
         for i, u in enumerate(units):
             u.times_ms.append(marks[s][i][0].elapsed_time(marks[s][i][1]))
+    # Units outside the step: their own loop, the same number of launches.
+    for u in extra:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record(stream)
+            u.launch()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        u.times_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
 
     traffic = read_traffic()
     rooflines = []
-    for u in units:
+    for u in all_units:
         avg_ms = sum(u.times_ms) / len(u.times_ms)
         med_ms = sorted(u.times_ms)[len(u.times_ms) // 2]
         achieved = u.work / (avg_ms * 1e-3) / (1e9 if u.unit == "GB/s" else 1e12)
@@ -234,17 +291,20 @@ def main():
             "bound": u.bound, "achieved": round(achieved, 2), "peak": u.peak, "unit": u.unit,
             "frac": round(achieved / u.peak, 4), "traffic": tr_bytes,
             "algorithmic": u.work, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5),
-            "min_ms": round(min(u.times_ms), 5), "max_ms": round(max(u.times_ms), 5)})
-    dominant = max(rooflines, key=lambda r: r["avg_ms"])
+            "min_ms": round(min(u.times_ms), 5), "max_ms": round(max(u.times_ms), 5),
+            "in_step": u.in_step})
+    in_step = [r for r in rooflines if r["in_step"]] or rooflines
+    dominant = max(in_step, key=lambda r: r["avg_ms"])
 
     sm = [r for r in rooflines if r["unit_name"].startswith("softmax")]
     at = [r for r in rooflines if r["unit_name"] == "attn"]
+    bw = [r for r in rooflines if r["unit_name"] == "attn_bwd"]
     if sm:
         sm_bytes = sum(r["algorithmic"] for r in sm)
         sm_ms = sum(r["avg_ms"] for r in sm)
         value, unit = sm_bytes / (sm_ms * 1e-3) / 1e9, "GB/s"
     else:
-        value, unit = at[0]["achieved"], "TFLOP/s"
+        value, unit = (at or bw)[0]["achieved"], "TFLOP/s"
 
     result = {
         "metric": METRIC,
@@ -275,6 +335,11 @@ def main():
         result["attention"] = {"value": at[0]["achieved"], "unit": "TFLOP/s",
                                "frac_of_bf16_peak": at[0]["frac"],
                                "flop_convention": "4*D per unmasked (query, key) pair"}
+    if bw:
+        result["attention_backward"] = {
+            "value": bw[0]["achieved"], "unit": "TFLOP/s", "frac_of_bf16_peak": bw[0]["frac"],
+            "avg_ms": bw[0]["avg_ms"], "in_step": False,
+            "flop_convention": "10*D per unmasked (query, key) pair (five products)"}
     if not args.no_cpu_baseline and args.only is None:
         result["cpu_baseline"] = cpu_baseline(torch, osm_inputs, args.cpu_budget)
         result["cpu_baseline"]["host_cpus"] = len(os.sched_getaffinity(0))
