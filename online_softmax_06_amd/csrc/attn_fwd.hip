@@ -30,13 +30,19 @@
 // S^T, so P needs no register shuffle.  Two LDS stages alternate; one barrier
 // per key tile.
 //
-// Exponent reference.  The reference m used in P = 2^(S' - m) is raised only
-// when a tile's row max exceeds it by more than kLag (in log2 units); P then
-// stays below 2^kLag, which float32 sums and bfloat16 P hold without loss of
-// range, and alpha is exactly 1 on most tiles, so the O rescale is skipped
-// whenever it is 1 for the whole wavefront.  In exact arithmetic the result
-// does not depend on the reference (the combine of §6.4.1 holds for any
-// finite one); the pages' recurrence is the special case kLag = 0.
+// Exponent reference.  In exact arithmetic the result does not depend on the
+// reference m used in P = 2^(S' - m): the combine of §6.4.1 holds for any
+// finite one, and the pages' recurrence (m = the running max) is one choice.
+// Here the masked sub-tiles at the end of a row compute the row max first and
+// raise the reference only when the max exceeds it by more than kLag (log2
+// units).  The unmasked sub-tiles compute no max at all: P is formed against
+// the current reference and summed, and only when a lane's partial sum
+// leaves [0, 2^64] (a score far above the reference) or a row has no finite
+// reference yet does the wavefront take the max, raise the reference, rescale
+// O and l and form P again.  P <= 2^64 keeps every float32 sum and product in
+// range and bfloat16 P loses no precision; alpha is 1 on almost every
+// sub-tile, so the O rescale is skipped whenever it is 1 for the whole
+// wavefront.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -298,67 +304,129 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
     read_k(1);
   }
   float p[16];
-  float m_new = 0.0f, ref = 0.0f, alpha = 1.0f;
-  constexpr int kExpRegions = kDC - 1;
+  float alpha = 1.0f;
+  float ps0 = 0.0f, ps1 = 0.0f;  // this lane's half of the sub-tile's row sum
+  if constexpr (kMask) {
+    // Masked sub-tiles (the last key tiles): the row max decides the new
+    // reference before any exponential.
+    float m_new = 0.0f, ref = 0.0f;
+    constexpr int kExpRegions = kDC - 1;
 #pragma unroll
-  for (int c = 0; c < kDC; ++c) {
-    if constexpr (kNext) {
-      if (c + 2 < kDC) read_k(c + 2);
-      sn = mfma32(ka[c % 3], st.qreg[c], sn);
-    }
-    // One global->LDS copy instruction per region (regions 1..): spread out,
-    // they do not queue up behind the other waves' copies.
-    if (c > 0) copy(c - 1);
-    if (c == 0) {
-      // A4: hide keys past the causal diagonal or past the valid keys.
-      if constexpr (kMask) {
+    for (int c = 0; c < kDC; ++c) {
+      if constexpr (kNext) {
+        if (c + 2 < kDC) read_k(c + 2);
+        sn = mfma32(ka[c % 3], st.qreg[c], sn);
+      }
+      // One global->LDS copy instruction per region (regions 1..): spread
+      // out, they do not queue up behind the other waves' copies.
+      if (c > 0) copy(c - 1);
+      if (c == 0) {
+        // A4: hide keys past the causal diagonal or past the valid keys.
         // Score i is key k0 + (i / 4) * 8 + half * 4 + i % 4: visible when
         // (i / 4) * 8 + i % 4 is below lim.
         const int lim = (kCausal ? min(kvlen, qrow + 1) : kvlen) - k0 - half * 4;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = (i >> 2) * 8 + (i & 3) < lim ? sc[i] : kNegInf;
+        // A5: row max over this lane's 16 keys and its partner's 16, the new
+        // exponent reference (raised only past kLag) and alpha.
+        float mx = max3(sc[0], sc[1], sc[2]);
+#pragma unroll
+        for (int i = 3; i < 15; i += 2) mx = max3(mx, sc[i], sc[i + 1]);
+        mx = __builtin_fmaxf(mx, sc[15]);
+        mx = __builtin_fmaxf(mx, swap_halves(mx));
+        const float mt = mx * scale_log2;
+        m_new = mt > st.m_run + kLag ? mt : st.m_run;
+        ref = finite_ref(m_new);
+        alpha = exp2_hw(st.m_run - ref);
+      } else {
+        // P = 2^(S * scale * log2 e - ref).
+        const int lo = (c - 1) * 16 / kExpRegions, hi = c * 16 / kExpRegions;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (i >= lo && i < hi) p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref));
+        }
       }
-      // A5: row max over this lane's 16 keys and its partner's 16, the new
-      // exponent reference (raised only past kLag) and alpha.
+      if (c == kDC - 1) {
+        read_v(0);
+        read_v(1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st.m_run = m_new;
+    // Keep the exponentials in phase 1: without this use the compiler sinks
+    // them past the rescale branch, next to the products that consume them.
+    asm volatile("" ::"v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]),
+                 "v"(p[6]), "v"(p[7]), "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]),
+                 "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
+    // Rescale the accumulator, skipped when alpha is 1 on every lane.
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+      // The empty asm keeps this a branch: without it the compiler would
+      // multiply unconditionally, since scaling by 1 is harmless.
+      asm volatile("");
+#pragma unroll
+      for (int b = 0; b < kDB; ++b) st.oacc[b] *= alpha;
+    }
+  } else {
+    // Unmasked sub-tiles: no row max.  P is formed against the current
+    // reference right away and summed; the reference moves only when a
+    // lane's partial sum leaves [0, 2^64] (a score far above the reference:
+    // too large for the sums, or +inf) or a row has no finite reference yet
+    // (its first sub-tile).  Any finite reference gives the same result in
+    // exact arithmetic, and P <= 2^64 keeps every sum and product in range.
+    const float ref = finite_ref(st.m_run);
+    constexpr int kPer = 16 / kDC;  // exponentials per region
+#pragma unroll
+    for (int c = 0; c < kDC; ++c) {
+      if constexpr (kNext) {
+        if (c + 2 < kDC) read_k(c + 2);
+        sn = mfma32(ka[c % 3], st.qreg[c], sn);
+      }
+      if (c > 0) copy(c - 1);
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) {
+        const int i = c * kPer + t;
+        p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref));
+        if (t & 1) ps1 += p[i]; else ps0 += p[i];
+      }
+      // Keep this region's exponentials and sums in the region.
+      asm volatile("" : "+v"(ps0), "+v"(ps1));
+      if (c == kDC - 1) {
+        read_v(0);
+        read_v(1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("" ::"v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]),
+                 "v"(p[6]), "v"(p[7]), "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]),
+                 "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
+    const bool settled = ps0 + ps1 <= 0x1p64f && st.m_run != kNegInf;
+    if (__builtin_amdgcn_ballot_w64(!settled) != 0) {
+      // Rare: the row max, a new reference (raised only past kLag), the
+      // rescale of O and l, and P again.
+      asm volatile("");
       float mx = max3(sc[0], sc[1], sc[2]);
 #pragma unroll
       for (int i = 3; i < 15; i += 2) mx = max3(mx, sc[i], sc[i + 1]);
       mx = __builtin_fmaxf(mx, sc[15]);
       mx = __builtin_fmaxf(mx, swap_halves(mx));
       const float mt = mx * scale_log2;
-      m_new = mt > st.m_run + kLag ? mt : st.m_run;
-      ref = finite_ref(m_new);
-      alpha = exp2_hw(st.m_run - ref);
-    } else {
-      // P = 2^(S * scale * log2 e - ref).
-      const int lo = (c - 1) * 16 / kExpRegions, hi = c * 16 / kExpRegions;
+      const float m_new = mt > st.m_run + kLag ? mt : st.m_run;
+      const float ref2 = finite_ref(m_new);
+      alpha = exp2_hw(st.m_run - ref2);
+      st.m_run = m_new;
+      ps0 = 0.0f;
+      ps1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (i >= lo && i < hi) p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref));
+        p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref2));
+        if (i & 1) ps1 += p[i]; else ps0 += p[i];
       }
-    }
-    if (c == kDC - 1) {
-      read_v(0);
-      read_v(1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  st.m_run = m_new;
-  // Keep the exponentials in phase 1: without this use the compiler sinks
-  // them past the rescale branch, next to the products that consume them.
-  asm volatile("" ::"v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]),
-               "v"(p[7]), "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]),
-               "v"(p[14]), "v"(p[15]));
-
-  // Phase 2 (A6): rescale the accumulator (skipped when alpha is 1 on every
-  // lane), then O^T += V^T P^T.
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-    // The empty asm keeps this a branch: without it the compiler would
-    // multiply unconditionally, since scaling by 1 is harmless.
-    asm volatile("");
 #pragma unroll
-    for (int b = 0; b < kDB; ++b) st.oacc[b] *= alpha;
+      for (int b = 0; b < kDB; ++b) st.oacc[b] *= alpha;
+    }
   }
+
+  // Phase 2 (A6): O^T += V^T P^T (and, on masked sub-tiles, the row sum).
   // P in the B-operand layout: slice kc2 holds scores kc2 * 8 + 0..7, i.e.
   // keys 16 kc2 + {0..3, 8..11} + 4 half, the order the V reads follow.
   bf16x8 pb[2];
@@ -369,18 +437,28 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
                            pack_bf16x2(p[o + 4], p[o + 5]), pack_bf16x2(p[o + 6], p[o + 7])));
   };
   pack_p(0);
-  float ps0 = 0.0f, ps1 = 0.0f;
-  constexpr int kAdds = 16 / kPV;  // scores summed per region
+  if constexpr (kMask) {
+    ps0 = p[0];
+    ps1 = p[1];
+  }
+  constexpr int kAdds = 16 / kPV;  // scores summed per region (masked sub-tiles)
 #pragma unroll
   for (int i = 0; i < kPV; ++i) {
     const int kc2 = i / kDB, b = i % kDB;
     if (i + 2 < kPV) read_v(i + 2);
     if (i == 0) pack_p(1);
     st.oacc[b] = mfma32(va[i % 3], pb[kc2], st.oacc[b]);
+    if constexpr (kMask) {
 #pragma unroll
-    for (int t = 0; t < kAdds; ++t) {
-      const int e = i * kAdds + t;
-      if (t & 1) ps1 += p[e]; else ps0 += p[e];
+      for (int t = 0; t < kAdds; ++t) {
+        const int e = i * kAdds + t;
+        if (e < 2) continue;
+        if (t & 1) ps1 += p[e]; else ps0 += p[e];
+      }
+      // Keep each region's share of the row sum in the region: otherwise the
+      // compiler defers the sums of several sub-tiles to the end of the loop
+      // body, where they run without products beside them and keep P live.
+      asm volatile("" : "+v"(ps0), "+v"(ps1));
     }
     __builtin_amdgcn_sched_barrier(0);
   }
