@@ -38,7 +38,8 @@ Parity status of each function is stated in its docstring.
 from .softmax_ref import masked_softmax_rows_ref, naive_softmax_rows_f32, softmax_rows_ref
 from .online_ref import EMPTY_STATE, all_trees, combine, online_state, tree_reduce
 from .attention_ref import attention_head_ref, attention_ref, blocked_attention_row_ref
-from .attention_bwd_ref import attention_bwd_head_ref, attention_bwd_ref, attention_probs_head_ref
+from .attention_bwd_ref import (attention_bwd_head_ref, attention_bwd_ref, attention_dq_rows_ref,
+                                attention_probs_head_ref)
 
 __all__ = [
     "softmax_rows_ref",
@@ -55,4 +56,5 @@ __all__ = [
     "attention_probs_head_ref",
     "attention_bwd_head_ref",
     "attention_bwd_ref",
+    "attention_dq_rows_ref",
 ]

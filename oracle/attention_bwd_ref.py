@@ -13,6 +13,9 @@ It is written with the softmax Jacobian, dP_ij/dS_ik = P_ij (delta_jk - P_ik),
 from the materialised probabilities; it does not use the output O or the
 log-sum-exp at all.
 
+``attention_dq_rows_ref`` gives dQ for chosen query rows only (rows are
+independent for dQ), for long sequences where the full P does not fit.
+
 Parity status: pinned.  ``attention_bwd_head_ref`` is checked against central
 finite differences of the (separately pinned) forward oracle, against torch's
 float64 CPU autograd of scaled_dot_product_attention, against closed forms
@@ -20,7 +23,8 @@ float64 CPU autograd of scaled_dot_product_attention, against closed forms
 gradient obeys: the key gradients sum to zero (scores are invariant to a shift
 of every key), the value gradients sum to the summed dO of the rows with a
 visible key (probability rows sum to one), and <dQ, Q> = <dK, K> (scores are
-invariant to Q -> t Q, K -> K / t).
+invariant to Q -> t Q, K -> K / t).  ``attention_dq_rows_ref`` is checked
+against the rows of ``attention_bwd_head_ref``.
 """
 
 import numpy as np
@@ -106,3 +110,29 @@ def attention_bwd_ref(q, k, v, do, scale, causal, heads=None, kv_len=None):
         return (dQ.reshape(B, H, N, D), dK.reshape(B, H, N, D),
                 dV.reshape(B, H, N, v.shape[3]))
     return dQ, dK, dV
+
+
+def attention_dq_rows_ref(q, k, v, do, scale, causal, rows):
+    """dQ of the given query rows of one (batch, head), float64.
+
+    The same definition as ``attention_bwd_head_ref`` restricted to those rows:
+    for row i, P_i = softmax of its scaled, masked scores, dP_i = V dO_i,
+    dS_i = P_i * (dP_i - P_i . dP_i), dQ_i = c dS_i K.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    c = _scale64(scale)
+    out = np.zeros((len(rows), q.shape[1]))
+    for n, i in enumerate(rows):
+        s = c * (k @ q[i])
+        if causal:
+            s[i + 1:] = -np.inf
+        m = np.max(s)
+        e = np.exp(s - m)
+        P = e / np.sum(e)
+        dP = v @ do[i]
+        dS = P * (dP - np.sum(P * dP))
+        out[n] = c * (dS @ k)
+    return out

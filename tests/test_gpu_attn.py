@@ -159,3 +159,28 @@ def test_no_reads_past_the_head(D, causal):
     torch.cuda.synchronize()
     assert not torch.isnan(o).any() and not torch.isnan(lse).any()
     compare(q, k, v, scale, causal, o, lse)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("slope,N", [(2.0, 300), (-2.0, 300), (6.0, 160), (-6.0, 160)])
+def test_reference_moves_with_the_scores(slope, N, D, causal):
+    # Scores that climb (or fall) steadily along the keys, `slope` log2 units
+    # per key: every 32-key sub-tile lies 64 (or 192) log2 units above the
+    # previous one, so the unmasked sub-tiles keep finding partial sums past
+    # 2^64 (or +inf) and must move their reference; falling scores underflow
+    # instead.  Magnitudes stay small enough that float32 scores keep the
+    # LSE within its tolerance.
+    B, H = 1, 2
+    _announce("reference moves", slope, N, D, causal)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    c = scale * math.log2(math.e)
+    g = torch.Generator().manual_seed(int(abs(slope) * 10) + N + D)
+    t = slope * torch.arange(N, dtype=torch.float32) / (c * D)
+    k = (t[None, None, :, None] * (1 + 0.05 * torch.randn(B, H, N, D, generator=g)))
+    q = torch.ones(B, H, N, D)
+    v = torch.randn(B, H, N, D, generator=g)
+    q, k, v = (x.to(torch.bfloat16).cuda() for x in (q, k, v))
+    o, lse = osm.attn_fwd(q, k, v, scale, causal)
+    torch.cuda.synchronize()
+    compare(q, k, v, scale, causal, o, lse)

@@ -27,7 +27,7 @@ import torch
 
 import online_softmax_06_amd as osm
 import osm_inputs
-from oracle import attention_bwd_head_ref, attention_ref
+from oracle import attention_bwd_head_ref, attention_dq_rows_ref, attention_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -186,3 +186,61 @@ def test_bwd_full_size_llama13b_sampled():
                     cfg["scale"], True, {"dq": dq[b, h].cpu(), "dk": dk[b, h].cpu(),
                                          "dv": dv[b, h].cpu()},
                     factor=4.0, o_from_forward=True)
+
+
+def test_bwd_small_config_full():
+    # The small workload (B1 H8 N1024 D64, non-causal) at full size, every head.
+    cfg = osm_inputs.attention_config("attn_small", device="cuda")
+    c = cfg["cfg"]
+    B, H, N, D = c["B"], c["H"], c["N"], c["D"]
+    _announce("attn_bwd small config", B, H, N, D)
+    q, k, v = cfg["q"], cfg["k"], cfg["v"]
+    do = osm_inputs.attention_grad_output(B, H, N, D, seed=c["seed"], device="cuda")
+    o, lse = osm.attn_fwd(q, k, v, cfg["scale"], cfg["causal"])
+    dq, dk, dv = osm.attn_bwd(q, k, v, o, lse, do, scale=cfg["scale"], causal=cfg["causal"])
+    torch.cuda.synchronize()
+    for h in range(H):
+        _check_head(q[0, h].cpu(), k[0, h].cpu(), v[0, h].cpu(), do[0, h].cpu(), None,
+                    cfg["scale"], cfg["causal"], {"dq": dq[0, h].cpu(), "dk": dk[0, h].cpu(),
+                                                  "dv": dv[0, h].cpu()},
+                    factor=4.0, o_from_forward=True)
+
+
+def test_bwd_long_context_sampled():
+    # The long-context workload (B1 H32 N16384 D128, causal, Q and K ~ 1.5
+    # N(0,1)) at full size: dQ of sampled rows of two heads against the
+    # oracle, dK and dV of every head against the two identities.
+    cfg = osm_inputs.attention_config("attn_long", device="cuda")
+    c = cfg["cfg"]
+    B, H, N, D = c["B"], c["H"], c["N"], c["D"]
+    _announce("attn_bwd long context", B, H, N, D)
+    q, k, v = cfg["q"], cfg["k"], cfg["v"]
+    do = osm_inputs.attention_grad_output(B, H, N, D, seed=c["seed"], device="cuda")
+    o, lse = osm.attn_fwd(q, k, v, cfg["scale"], True)
+    dq, dk, dv = osm.attn_bwd(q, k, v, o, lse, do, scale=cfg["scale"], causal=True)
+    torch.cuda.synchronize()
+    dk_sum = dk.float().sum(dim=2)
+    dv_sum = dv.float().sum(dim=2)
+    do_sum = do.float().sum(dim=2)
+    assert dk_sum.abs().max().item() < 0.05 * dk.float().abs().sum(dim=2).max().item() + 1e-3
+    assert (dv_sum - do_sum).abs().max().item() < 4 * U * do.float().abs().sum(dim=2).max().item()
+    rows = [0, 1, 63, 64, 1000, 8191, 8192, 12345, N - 2, N - 1]
+    for h in (0, H - 1):
+        _announce("  head", h)
+        qh, kh, vh, gh, oh = (t[0, h].double().cpu().numpy() for t in (q, k, v, do, o))
+        ref = attention_dq_rows_ref(qh, kh, vh, gh, cfg["scale"], True, rows)
+        got = dq[0, h].double().cpu().numpy()[rows]
+        # The dQ bound of the module docstring, row by row, with |O| taken as
+        # P |V| (the library's forward output) and factor 4.
+        c32 = float(np.float32(cfg["scale"]))
+        for n, i in enumerate(rows):
+            s = c32 * (kh[:i + 1] @ qh[i])
+            P = np.exp(s - s.max())
+            P /= P.sum()
+            dP = vh[:i + 1] @ gh[i]
+            dS = P * (dP - np.sum(P * dP))
+            A = np.sum(np.abs(gh[i]) * (P @ np.abs(vh[:i + 1])))
+            bound = 4 * U * (c32 * ((np.abs(dS) + P * A) @ np.abs(kh[:i + 1])) + np.abs(ref[n]))
+            err = np.abs(got[n] - ref[n])
+            assert (err <= bound + 1e-30).all(), (h, i, float(err.max()),
+                                                   float((err / (bound + 1e-30)).max()))

@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_bwd_head_ref, attention_bwd_ref, attention_head_ref
+from oracle import (attention_bwd_head_ref, attention_bwd_ref, attention_dq_rows_ref,
+                    attention_head_ref)
 
 
 def _rand(shape, seed, sigma=1.0):
@@ -110,3 +111,13 @@ def test_invariants(causal):
     np.testing.assert_allclose(dV.sum(axis=0), do.sum(axis=0), atol=1e-12)
     # S is unchanged by Q -> tQ, K -> K/t.
     assert abs(np.sum(dQ * q) - np.sum(dK * k)) < 1e-11
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dq_rows_match_the_full_gradient(causal):
+    n, d = 50, 6
+    q, k, v, do = (_rand((n, d), s) for s in (51, 52, 53, 54))
+    dQ, _, _ = attention_bwd_head_ref(q, k, v, do, 0.7, causal)
+    rows = [0, 1, 17, 49]
+    np.testing.assert_allclose(attention_dq_rows_ref(q, k, v, do, 0.7, causal, rows), dQ[rows],
+                               atol=1e-13, rtol=0)
