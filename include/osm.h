@@ -259,8 +259,24 @@ int osm_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int D,
                  float scale, int causal, void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Bytes of workspace osm_attn_bwd needs: 8 * B * H * (N rounded up to a
- * multiple of 128); -1 for invalid arguments. */
+/*
+ * osm_attn_bwd_ex -- osm_attn_bwd for a forward run with key padding
+ * (osm_attn_fwd_ex with the same kv_len and no bias).
+ *
+ *   kv_len   device pointer to int32 [B] (valid keys per batch, clamped to
+ *            [0, N]), or NULL for N.  Keys at or past a batch's length get
+ *            dk = dv = 0 and contribute nothing to dq; key blocks wholly
+ *            past the length are not visited.
+ *
+ * Returns as osm_attn_bwd, plus OSM_ERR_INVALID_ARG for a misaligned kv_len.
+ */
+int osm_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int D,
+                    float scale, int causal, const int32_t* kv_len, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace osm_attn_bwd and osm_attn_bwd_ex need: 8 * B * H * (N
+ * rounded up to a multiple of 128); -1 for invalid arguments. */
 int64_t osm_attn_bwd_workspace(int B, int H, int N, int D);
 
 /* Human-readable name of a status code; never NULL, static storage. */

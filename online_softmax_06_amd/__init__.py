@@ -22,6 +22,8 @@ ints; ``stream`` is a hipStream_t handle, 0 for the null stream):
     osm_attn_fwd_split_workspace(B, H, N, D, splits) -> bytes
     osm_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale, causal,
                  workspace, workspace_bytes, stream) -> status
+    osm_attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
+                    causal, kv_len, workspace, workspace_bytes, stream) -> status
     osm_attn_bwd_workspace(B, H, N, D) -> bytes
     osm_status_string(status) -> str
 
@@ -30,7 +32,8 @@ Tensor-level helpers:
     softmax_rows(x, out=None, mask=None, row_len=None, split=False) -> Tensor
     attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None,
              kv_len=None, bias=None, splits=1) -> (o, lse)
-    attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False) -> (dq, dk, dv)
+    attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, kv_len=None)
+             -> (dq, dk, dv)
 
 If the library has not been built, every call raises ``RuntimeError``; there
 is no fallback implementation.
@@ -45,7 +48,7 @@ __all__ = [
     "OsmError", "lib_path", "load_library", "osm_softmax_rows", "osm_softmax_rows_ex",
     "osm_softmax_rows_split", "osm_softmax_rows_split_workspace",
     "osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split", "osm_attn_fwd_split_workspace",
-    "osm_attn_bwd", "osm_attn_bwd_workspace",
+    "osm_attn_bwd", "osm_attn_bwd_ex", "osm_attn_bwd_workspace",
     "osm_status_string", "osm_version", "softmax_rows",
     "attn_fwd", "attn_bwd",
 ]
@@ -105,6 +108,9 @@ def load_library():
     lib.osm_attn_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int,
                                  c_int, c_int, c_int, c_f, c_int, c_vp, c_i64, c_vp]
     lib.osm_attn_bwd.restype = c_int
+    lib.osm_attn_bwd_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int,
+                                    c_int, c_int, c_int, c_f, c_int, c_vp, c_vp, c_i64, c_vp]
+    lib.osm_attn_bwd_ex.restype = c_int
     lib.osm_attn_bwd_workspace.argtypes = [c_int, c_int, c_int, c_int]
     lib.osm_attn_bwd_workspace.restype = c_i64
     lib.osm_status_string.argtypes = [c_int]
@@ -167,6 +173,12 @@ def osm_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale, causal, w
                  workspace_bytes, stream=0):
     return load_library().osm_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
                                        int(causal), workspace, workspace_bytes, stream)
+
+
+def osm_attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale, causal, kv_len,
+                    workspace, workspace_bytes, stream=0):
+    return load_library().osm_attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
+                                          int(causal), kv_len, workspace, workspace_bytes, stream)
 
 
 def osm_attn_bwd_workspace(B, H, N, D):
@@ -317,12 +329,13 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None,
     return out, lse
 
 
-def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None):
+def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None,
+             kv_len=None):
     """Attention backward on contiguous bfloat16 [B, H, N, D] CUDA tensors.
 
     ``o`` and ``lse`` are the forward's outputs for ``q, k, v`` with the same
-    ``scale`` and ``causal``; ``dout`` is the gradient of the loss with respect
-    to ``o``.  Returns ``(dq, dk, dv)`` (bfloat16, shaped like q).  The
+    ``scale``, ``causal`` and ``kv_len`` (int32 CUDA tensor [B], or None);
+    ``dout`` is the gradient of the loss with respect to ``o``.  Returns ``(dq, dk, dv)`` (bfloat16, shaped like q).  The
     workspace is allocated here, through torch's caching allocator.
     """
     torch = _torch()
@@ -344,14 +357,20 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, 
         elif t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous bfloat16 tensor shaped like q")
         grads.append(t)
+    len_ptr = 0
+    if kv_len is not None:
+        if not kv_len.is_cuda or kv_len.dtype != torch.int32 or kv_len.numel() != B \
+                or not kv_len.is_contiguous():
+            raise ValueError("kv_len must be a contiguous int32 CUDA tensor of length B")
+        len_ptr = kv_len.data_ptr()
     need = osm_attn_bwd_workspace(B, H, N, D)
     if need < 0:
         raise OsmError(OSM_ERR_INVALID_ARG, "osm_attn_bwd_workspace")
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    st = osm_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                      dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
-                      grads[2].data_ptr(), B, H, N, D, float(scale), bool(causal),
-                      ws.data_ptr(), ws.numel(), _stream_handle(q.device))
+    st = osm_attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                         grads[2].data_ptr(), B, H, N, D, float(scale), bool(causal), len_ptr,
+                         ws.data_ptr(), ws.numel(), _stream_handle(q.device))
     if st != OSM_OK:
-        raise OsmError(st, "osm_attn_bwd")
+        raise OsmError(st, "osm_attn_bwd_ex")
     return tuple(grads)

@@ -332,7 +332,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int BH, int N, int Np, float scale, float scale_log2) {
+    uint16_t* __restrict__ dv, int BH, int H, int N, int Np, const int32_t* __restrict__ kv_len,
+    float scale, float scale_log2) {
   using G = Geo<D>;
   constexpr int kDC = G::kDC, kDB = G::kDB;
   constexpr int kSub = 32;  // query rows per streamed tile
@@ -360,6 +361,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
   const int head_bytes = N * D * 2;
   const int kw = kb * kBlk + wave * 32;  // first key of this wave
   const int key = kw + col;              // this lane's key
+  // Keys at or past the batch's key length are hidden from every row.
+  const int kvlen = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
+  f32x16 dka[kDB], dva[kDB];
+#pragma unroll
+  for (int b = 0; b < kDB; ++b) dka[b] = dva[b] = f32x16{};
+  // A block wholly past the key length has dK = dV = 0 (uniform over the
+  // workgroup: no barrier is skipped by part of it).
+  if (kb * kBlk < kvlen) {
 
   {
     int koff[KCopy::kPerWave];
@@ -373,9 +382,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
     const int64_t e = head + (int64_t)key * D + c * 16 + half * 8;
     vreg[c] = key < N ? *reinterpret_cast<const bf16x8*>(v + e) : bf16x8{};
   }
-  f32x16 dka[kDB], dva[kDB];
-#pragma unroll
-  for (int b = 0; b < kDB; ++b) dka[b] = dva[b] = f32x16{};
 
   int coff[QCopy::kPerWave];
   QCopy::offsets(wave, lane, coff);
@@ -402,8 +408,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
                      const float* eb, int t) __attribute__((always_inline)) {
     constexpr bool kMasked = decltype(masked)::value;
     const int qbase = t * kSub;  // first query row of the tile
-    // Causal: every query row of the tile is before this wave's keys.
-    if (kMasked && kw > qbase + 31) return;
+    // Masked tiles: skip when every key of this wave is hidden from every
+    // row of the tile (causal: all rows before the keys; or all keys past
+    // the key length).
+    if (kMasked && ((kCausal && kw > qbase + 31) || kw >= kvlen)) return;
     f32x16 sc = f32x16{}, dp = f32x16{};
     {
       constexpr int kAhead = 1, kBuf = kAhead + 1;
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * j + r;
         float x = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -l4[r]));
-        if (kMasked && rho(i) < lim) x = 0.0f;
+        if (kMasked && ((kCausal && rho(i) < lim) || key >= kvlen)) x = 0.0f;
         sc[i] = x;
         dp[i] = x * (dp[i] - e4[r]);
       }
@@ -472,19 +480,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
 
   issue(qs0, gs0, ls0, es0, t_begin);
   int t = t_begin;
-  if constexpr (kCausal) {
-    // The four tiles over the block's own key range cross the diagonal.
-    step(Masked{}, Stage0{}, t);
-    if (t + 1 < nst) step(Masked{}, Stage1{}, t + 1);
-    if (t + 2 < nst) step(Masked{}, Stage0{}, t + 2);
-    if (t + 3 < nst) step(Masked{}, Stage1{}, t + 3);
-    t += 4;
+  if (kb * kBlk + kBlk > kvlen) {
+    // The block holds the key length: every tile masks its keys.
+    for (; t + 1 < nst; t += 2) {
+      step(Masked{}, Stage0{}, t);
+      step(Masked{}, Stage1{}, t + 1);
+    }
+    if (t < nst) step(Masked{}, Stage0{}, t);
+  } else {
+    if constexpr (kCausal) {
+      // The four tiles over the block's own key range cross the diagonal.
+      step(Masked{}, Stage0{}, t);
+      if (t + 1 < nst) step(Masked{}, Stage1{}, t + 1);
+      if (t + 2 < nst) step(Masked{}, Stage0{}, t + 2);
+      if (t + 3 < nst) step(Masked{}, Stage1{}, t + 3);
+      t += 4;
+    }
+    for (; t + 1 < nst; t += 2) {
+      step(Plain{}, Stage0{}, t);
+      step(Plain{}, Stage1{}, t + 1);
+    }
+    if (t < nst) step(Plain{}, Stage0{}, t);
   }
-  for (; t + 1 < nst; t += 2) {
-    step(Plain{}, Stage0{}, t);
-    step(Plain{}, Stage1{}, t + 1);
-  }
-  if (t < nst) step(Plain{}, Stage0{}, t);
+  }  // kb * kBlk < kvlen
 
   // dK^T and dV^T: lane = key, register i of block b = dim 32 b + 8 (i / 4)
   // + 4 half + i % 4.
@@ -511,7 +529,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dq,
-    int BH, int N, int Np, float scale, float scale_log2) {
+    int BH, int H, int N, int Np, const int32_t* __restrict__ kv_len, float scale,
+    float scale_log2) {
   using G = Geo<D>;
   constexpr int kDC = G::kDC, kDB = G::kDB;
   __shared__ __attribute__((aligned(1024))) char ks0[G::kBytes];
@@ -551,11 +570,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   KVCopy::offsets(wave, lane, coff);
   const ReadOffsets<D> off = read_offsets<D>(lane);
 
-  const int nkt = (N + kTile - 1) / kTile;
+  // Keys at or past the batch's key length are hidden from every row.
+  const int kvlen = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
+  const int nkt = (kvlen + kTile - 1) / kTile;
   // Causal: keys past the block's last query row are hidden from all of it.
   const int t_end = kCausal ? min(nkt, (qt + 1) * (kBlk / kTile)) : nkt;
   // The last key visible from this lane's row, plus one.
-  const int vis_end = kCausal ? min(qrow + 1, N) : N;
+  const int vis_end = kCausal ? min(qrow + 1, kvlen) : kvlen;
 
   auto issue = [&](char* kbuf, char* vbuf, int t) __attribute__((always_inline)) {
     KVCopy::issue(kbuf, k + head, head_bytes, t * kTile, wave, coff);
@@ -569,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       const int r0 = s * 32;
       const int kbase = t * kTile + r0;  // first key of the sub-tile
       // Masked tiles: every key of the sub-tile is hidden from this wave.
-      if (kMasked && (kbase >= N || (kCausal && kbase > qw + 31))) continue;
+      if (kMasked && (kbase >= kvlen || (kCausal && kbase > qw + 31))) continue;
       f32x16 sc, dp;
       first_products<D, 1>(kbuf, vbuf, off, r0, qreg, oreg, sc, dp);
       // Key kbase + 4 half + rho is visible from this row when rho < lim.
@@ -589,13 +610,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   using Masked = std::integral_constant<bool, true>;
   using Plain = std::integral_constant<bool, false>;
   // Masked tiles: those crossing the causal diagonal or the end of the keys.
-  const int t_plain_end = min(kCausal ? qt * (kBlk / kTile) : nkt, N / kTile);
+  const int t_plain_end = min(kCausal ? qt * (kBlk / kTile) : nkt, kvlen / kTile);
   auto run = [&](const char* kbuf, const char* vbuf, int t) __attribute__((always_inline)) {
     if (t >= t_plain_end) compute(Masked{}, kbuf, vbuf, t);
     else compute(Plain{}, kbuf, vbuf, t);
   };
 
-  issue(ks0, vs0, 0);
+  if (t_end > 0) issue(ks0, vs0, 0);
   for (int t = 0; t < t_end; t += 2) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -622,8 +643,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 
 template <int D, bool kCausal>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                      const void* dout, void* dq, void* dk, void* dv, int BH, int N, float scale,
-                      void* workspace, hipStream_t stream) {
+                      const void* dout, void* dq, void* dk, void* dv, int BH, int H, int N,
+                      float scale, const int32_t* kv_len, void* workspace, hipStream_t stream) {
   const int Np = (N + kPad - 1) / kPad * kPad;
   float* delta = static_cast<float*>(workspace);
   float* lse2 = delta + (int64_t)BH * Np;
@@ -638,9 +659,10 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   const unsigned blocks = (unsigned)((int64_t)BH * ((N + kBlk - 1) / kBlk));
   attn_bwd_dkdv_kernel<D, kCausal><<<dim3(blocks), dim3(kThreads), 0, stream>>>(
       q16, k16, v16, g16, lse2, delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), BH,
-      N, Np, scale, scale_log2);
+      H, N, Np, kv_len, scale, scale_log2);
   attn_bwd_dq_kernel<D, kCausal><<<dim3(blocks), dim3(kThreads), 0, stream>>>(
-      q16, k16, v16, g16, lse2, delta, static_cast<uint16_t*>(dq), BH, N, Np, scale, scale_log2);
+      q16, k16, v16, g16, lse2, delta, static_cast<uint16_t*>(dq), BH, H, N, Np, kv_len, scale,
+      scale_log2);
   return hipGetLastError();
 }
 
@@ -653,19 +675,19 @@ int64_t attn_bwd_workspace(int B, int H, int N) {
 
 hipError_t attn_bwd_launch(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
-                           int H, int N, int D, float scale, bool causal, void* workspace,
-                           hipStream_t stream) {
+                           int H, int N, int D, float scale, bool causal, const int32_t* kv_len,
+                           void* workspace, hipStream_t stream) {
   const int BH = B * H;
   if (D == 128) {
-    return causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, N, scale,
-                                          workspace, stream)
-                  : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, N, scale,
-                                           workspace, stream);
+    return causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, H, N, scale,
+                                          kv_len, workspace, stream)
+                  : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, H, N, scale,
+                                           kv_len, workspace, stream);
   }
-  return causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, N, scale, workspace,
-                                       stream)
-                : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, N, scale,
-                                        workspace, stream);
+  return causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, H, N, scale, kv_len,
+                                       workspace, stream)
+                : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, H, N, scale,
+                                        kv_len, workspace, stream);
 }
 
 }  // namespace osm

@@ -170,10 +170,11 @@ int64_t osm_attn_bwd_workspace(int B, int H, int N, int D) {
   return osm::attn_bwd_workspace(B, H, N);  // < 8 * 2^31 * 2^31: no overflow
 }
 
-int osm_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                 const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int D,
-                 float scale, int causal, void* workspace, int64_t workspace_bytes, void* stream) {
-  const int st = check_attn(q, k, v, o, lse, B, H, N, D, scale, nullptr, nullptr, 0, 0, 1);
+int osm_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int D,
+                    float scale, int causal, const int32_t* kv_len, void* workspace,
+                    int64_t workspace_bytes, void* stream) {
+  const int st = check_attn(q, k, v, o, lse, B, H, N, D, scale, kv_len, nullptr, 0, 0, 1);
   if (st != OSM_OK || (int64_t)B * H * N == 0) return st;
   if (!dout || !dq || !dk || !dv) return OSM_ERR_INVALID_ARG;
   if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
@@ -182,7 +183,15 @@ int osm_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (need < 0 || workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
     return OSM_ERR_INVALID_ARG;
   return from_hip(osm::attn_bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
-                                       causal != 0, workspace, static_cast<hipStream_t>(stream)));
+                                       causal != 0, kv_len, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int osm_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int D,
+                 float scale, int causal, void* workspace, int64_t workspace_bytes, void* stream) {
+  return osm_attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale, causal, nullptr,
+                         workspace, workspace_bytes, stream);
 }
 
 int osm_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

@@ -43,11 +43,12 @@ hipError_t attn_fwd_split_launch(const void* q, const void* k, const void* v, vo
 
 // Attention backward: workspace bytes (Delta and LSE * log2 e per query row,
 // float32, rows padded to a multiple of 128 per head), and the launch of the
-// three kernels (prep, dK/dV, dQ).  D must be 64 or 128.
+// three kernels (prep, dK/dV, dQ).  D must be 64 or 128; kv_len (nullable,
+// int32 [B]) limits the keys of each batch as in the forward.
 int64_t attn_bwd_workspace(int B, int H, int N);
 hipError_t attn_bwd_launch(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
-                           int H, int N, int D, float scale, bool causal, void* workspace,
-                           hipStream_t stream);
+                           int H, int N, int D, float scale, bool causal, const int32_t* kv_len,
+                           void* workspace, hipStream_t stream);
 
 }  // namespace osm

@@ -31,7 +31,7 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["osm_attn_bwd", "osm_attn_bwd_workspace",
+    assert _declared_functions() == ["osm_attn_bwd", "osm_attn_bwd_ex", "osm_attn_bwd_workspace",
                                      "osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split",
                                      "osm_attn_fwd_split_workspace", "osm_softmax_rows",
                                      "osm_softmax_rows_ex", "osm_softmax_rows_split",
@@ -203,3 +203,11 @@ def _bwd(B=1, H=2, N=300, D=128, scale=0.1, causal=1, ptrs=None, ws=FAKE, wsb=1 
 ])
 def test_attn_bwd_argument_checks(lib, kw, expect):
     assert _bwd(**kw) == expect
+
+
+def test_attn_bwd_ex_checks_kv_len_alignment(lib):
+    p = [FAKE] * 9
+    assert osm.osm_attn_bwd_ex(*p, 1, 2, 300, 128, 0.1, 1, FAKE + 2, FAKE, 1 << 30, 0) == \
+        osm.OSM_ERR_INVALID_ARG
+    assert osm.osm_attn_bwd_ex(*p, 1, 2, 300, 96, 0.1, 1, 0, FAKE, 1 << 30, 0) == \
+        osm.OSM_ERR_UNSUPPORTED

@@ -51,16 +51,18 @@ def _inputs(B, H, N, D, seed, qk_sigma=1.0):
     return q, k, v, do
 
 
-def _oracle_fwd(q, k, v, scale, causal):
-    O, L = attention_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale, causal)
+def _oracle_fwd(q, k, v, scale, causal, kv_len=None):
+    O, L = attention_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale, causal,
+                         kv_len=kv_len)
     return (torch.from_numpy(O).to(torch.bfloat16), torch.from_numpy(L).to(torch.float32))
 
 
-def _check_head(qh, kh, vh, doh, oh, scale, causal, got, factor=2.0, o_from_forward=False):
+def _check_head(qh, kh, vh, doh, oh, scale, causal, got, factor=2.0, o_from_forward=False,
+                kv_len=None):
     """Compare one head's (dq, dk, dv) with the oracle within the bound above."""
     q64, k64, v64, do64 = (t.double().numpy() for t in (qh, kh, vh, doh))
     dQ, dK, dV, P, dS = attention_bwd_head_ref(q64, k64, v64, do64, scale, causal,
-                                               return_probs=True)
+                                               kv_len=kv_len, return_probs=True)
     c = float(np.float32(scale))
     if o_from_forward:
         A = np.sum(np.abs(do64) * (P @ np.abs(v64)), axis=1)
@@ -244,3 +246,27 @@ def test_bwd_long_context_sampled():
             err = np.abs(got[n] - ref[n])
             assert (err <= bound + 1e-30).all(), (h, i, float(err.max()),
                                                    float((err / (bound + 1e-30)).max()))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_kv_len(D, causal):
+    # Key padding: a full batch, a length inside a key block, no keys at all,
+    # a short one.  Hidden keys get dk = dv = 0; rows without a visible key
+    # (LSE = -inf) contribute nothing.
+    B, H, N = 4, 2, 300
+    lens = [300, 129, 0, 37]
+    _announce("attn_bwd kv_len", B, H, N, D, causal, lens)
+    q, k, v, do = _inputs(B, H, N, D, seed=31 + D + int(causal))
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = _oracle_fwd(q, k, v, scale, causal, kv_len=np.array(lens))
+    dev = [t.cuda() for t in (q, k, v, o, lse, do)]
+    dq, dk, dv = osm.attn_bwd(*dev, scale=scale, causal=causal,
+                              kv_len=torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for b in range(B):
+        assert (dk[b, :, lens[b]:] == 0).all() and (dv[b, :, lens[b]:] == 0).all()
+        for h in range(H):
+            _check_head(q[b, h], k[b, h], v[b, h], do[b, h], o[b, h], scale, causal,
+                        {"dq": dq[b, h].cpu(), "dk": dk[b, h].cpu(), "dv": dv[b, h].cpu()},
+                        kv_len=lens[b])
