@@ -17,11 +17,11 @@
 // Three launches, no atomics (the result is deterministic):
 //   prep  Delta and LSE * log2 e per query row into a padded workspace
 //         (padding rows get Delta = 0 and +inf, so their P is exactly 0);
-//   dkdv  a workgroup owns 128 keys (32 per wavefront), keeps their K and V
-//         fragments and the dK^T, dV^T accumulators in registers and streams
-//         the 64-row tiles of Q and dO (plus their Delta and LSE) through
-//         LDS: per 32-row sub-tile S = Q K^T, dP = dO V^T, P, dS, then
-//         dV^T += dO^T P and dK^T += Q^T dS;
+//   dkdv  a workgroup owns 128 keys (32 per wavefront), keeps their K rows
+//         in LDS, their V fragments and the dK^T, dV^T accumulators in
+//         registers, and streams 32-row tiles of Q and dO (plus their Delta
+//         and LSE) through LDS: per tile S = Q K^T, dP = dO V^T, P, dS, then
+//         dV^T += dO^T P and dK^T += Q^T dS (two workgroups per CU);
 //   dq    a workgroup owns 128 query rows (32 per wavefront), keeps Q, dO,
 //         Delta, LSE and the dQ^T accumulator in registers and streams the
 //         64-key tiles of K and V: S^T = K Q^T, dP^T = V dO^T, P, dS, then
@@ -68,7 +68,8 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Geometry of a streamed tile of kTile rows x D bfloat16, row-major in LDS.
+// Geometry of the streamed tiles: rows of D bfloat16, row-major in LDS, with
+// 16-byte units swizzled per row (kBytes: one kTile-row tile).
 template <int D>
 struct Geo {
   static constexpr int kUnits = D / 8;     // 16-byte units per row
