@@ -1,6 +1,6 @@
 /*
- * osm.h -- C ABI of libosm: online softmax and the fused attention forward
- * on AMD Instinct MI355X (gfx950).
+ * osm.h -- C ABI of libosm: online softmax, the fused attention forward and
+ * its backward on AMD Instinct MI355X (gfx950).
  *
  * Sources of the operations (cited by page title and section):
  *   [Ch6]   "Ch.6 Softmax and Online Softmax", yangyitao.com CUDA
