@@ -3,7 +3,7 @@
 // only in registers.
 //
 // Method ("Ch.6 Softmax and Online Softmax" §6.5-§6.6; xxqk §4.1): a workgroup
-// owns a tile of 128 query rows and streams the key/value tiles of its
+// owns a tile of 128 or 256 query rows and streams the key/value tiles of its
 // (batch, head) through LDS.  Per tile it forms the scores on the matrix
 // cores, updates the running max m and rescaled sum l of every query row,
 // rescales the output accumulator by alpha = 2^(m_old - m_new), and adds
@@ -56,11 +56,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128;     // query rows per workgroup
 constexpr int kBN = 64;      // keys per tile
-constexpr int kWaves = 4;    // wavefronts per workgroup, 32 query rows each
-constexpr int kThreads = kWaves * 64;
 constexpr float kLag = 8.0f;  // allowed lag of the exponent reference (log2 units)
+
+// Workgroup shape: kW wavefronts of 32 query rows each.  With kW = 4 two
+// workgroups share a CU; with kW = 8 (D = 128 only: a K sub-tile must give
+// every wavefront a copy instruction) one workgroup fills it, two
+// wavefronts per SIMD.  Both have two wavefronts per SIMD, but with two
+// workgroups the one dispatched second runs about a fifth slower on the same
+// work and sets the end of a persistent launch; with one workgroup the two
+// wavefronts of a SIMD advance together and every K/V tile in LDS serves
+// twice the rows.  Its 256-row query tiles cost more on the causal diagonal,
+// where a wavefront idles over the sub-tiles above its rows, so the launch
+// takes kW = 8 for long or unmasked rows and kW = 4 for short causal rows.
+template <int D, int kW>
+struct Shape {
+  static_assert(kW == 4 || (kW == 8 && D == 128), "supported shapes");
+  static constexpr int kWaves = kW;
+  static constexpr int kThreads = kW * 64;
+  static constexpr int kBM = kW * 32;          // query rows per workgroup
+  static constexpr int kPerCU = kW == 8 ? 1 : 2;  // resident workgroups per CU
+};
 
 // Buffer descriptor word 3 for raw (untyped) buffer loads on gfx950.
 constexpr int kBufferFlags = 0x00020000;
@@ -76,7 +92,6 @@ template <int D>
 struct Tile {
   static constexpr int kUnits = D / 8;                // 16-byte units per key row
   static constexpr int kBytes = kBN * D * 2;          // one K or V tile
-  static constexpr int kLoadsPerWave = kBN * kUnits / 64 / kWaves;  // 1 KB each
   // Row swizzles of the 16-byte units (LDS has 64 four-byte banks).
   // K rows are read 16 bytes per lane, 16 consecutive rows per 256-byte bank
   // sweep: XOR by row & 15 (row & 7 at D = 64) spreads them over all banks.
@@ -98,10 +113,10 @@ struct Tile {
 // buffer descriptor starts at row k0 and ends with the head, so rows at or
 // past the end of the head fall outside its range and arrive as zeros; k0 =
 // N turns an instruction into a zero fill without memory traffic.
-template <int D, int kRows>
+template <int D, int kRows, int kW>
 struct RowCopy {
   static constexpr int kUnits = D / 8;
-  static constexpr int kPerWave = kRows * kUnits / 64 / kWaves;
+  static constexpr int kPerWave = kRows * kUnits / 64 / kW;
   static_assert(kPerWave >= 1, "every wave issues at least one load");
   template <int (*Swz)(int)>
   __device__ static int lane_offset(int wave, int lane, int i) {
@@ -552,8 +567,8 @@ __device__ __forceinline__ int item_of(const Schedule& sc, int g, int k, int BH,
 // key tiles and writes a partial result normalised by its own l -- O_s in
 // float32 and LSE_s -- to o_part / lse_part; attn_split_merge_kernel combines
 // the splits.
-template <int D, bool kCausal, bool kBias, bool kSplit>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
+template <int D, int kW, bool kCausal, bool kBias, bool kSplit>
+__global__ __launch_bounds__((Shape<D, kW>::kThreads), (Shape<D, kW>::kPerCU)) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int BH,
     int H, int N, float scale_log2, AttnOptions opt, Schedule sched, int splits,
@@ -581,8 +596,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int half = lane >> 5;  // which 8-element half of each 16-wide slice
   const int head_bytes = N * D * 2;
   const LaneOffsets<D> off = lane_offsets<D>(lane);
-  using KCopy = RowCopy<D, 32>;
-  using VCopy = RowCopy<D, 64>;
+  using KCopy = RowCopy<D, 32, kW>;
+  using VCopy = RowCopy<D, 64, kW>;
   static_assert(2 * KCopy::kPerWave <= kDC - 1 && VCopy::kPerWave <= kDC - 1,
                 "a sub-step has a phase-1 region for each of its copies");
   int koff[KCopy::kPerWave], voff[VCopy::kPerWave];
@@ -605,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const int64_t head_off = (int64_t)bh * N * D;
     const uint16_t* kh = k + head_off;
     const uint16_t* vh = v + head_off;
-    const int q0 = qt * kBM;
+    const int q0 = qt * Shape<D, kW>::kBM;
     const int qw = q0 + wave * 32;  // first query row of this wave
     const int qrow = qw + col;      // this lane's query row
     const int b = bh / H, h = bh % H;
@@ -614,7 +629,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                                     (int64_t)min(qrow, N - 1) * N
                               : nullptr;
 
-    const int kv_end = kCausal ? min(kvlen, q0 + kBM) : kvlen;
+    const int kv_end = kCausal ? min(kvlen, q0 + Shape<D, kW>::kBM) : kvlen;
     const int ntiles_all = (kv_end + kBN - 1) / kBN;
     // Key tiles [j_begin, j_end) of this item (all of them without splits).
     int j_begin = 0, j_end = ntiles_all;
@@ -841,11 +856,12 @@ int device_cus() {
   return cached[dev];
 }
 
-template <int D, bool kCausal, bool kBias, bool kSplit>
+template <int D, int kW, bool kCausal, bool kBias, bool kSplit>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int H,
                   int N, float scale, const AttnOptions& opt, int splits, float* o_part,
                   float* lse_part, hipStream_t s) {
-  const int nqt = (N + kBM - 1) / kBM;
+  using Sh = Shape<D, kW>;
+  const int nqt = (N + Sh::kBM - 1) / Sh::kBM;
   const float scale_log2 = scale * kLog2e;
   Schedule sc;
   sc.nqt = nqt;
@@ -857,8 +873,8 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     sc.workers = 0;
     grid = (int64_t)nqt * BH * splits;
   } else {
-    // Two resident workgroups per compute unit.
-    const int slots = 2 * device_cus();
+    // Resident workgroups: Sh::kPerCU per compute unit.
+    const int slots = Sh::kPerCU * device_cus();
     if ((BH & 7) == 0 && slots >= 8) {
       sc.mode = kPairsXcd;
       const int64_t per_xcd = (int64_t)sc.heads_per_xcd * sc.pairs;
@@ -871,8 +887,8 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
       grid = sc.workers;
     }
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<D, kCausal, kBias, kSplit>), dim3((unsigned)grid),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, kW, kCausal, kBias, kSplit>), dim3((unsigned)grid),
+                     dim3(Sh::kThreads), 0, s, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<uint16_t*>(o), lse, BH, H, N, scale_log2, opt, sc, splits, o_part,
                      lse_part);
@@ -891,15 +907,27 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
                     int H, int N, float scale, bool causal, const AttnOptions& opt, int splits,
                     float* o_part, float* lse_part, hipStream_t s) {
   if (opt.bias != nullptr) {
-    return causal ? launch<D, true, true, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
-                                                  o_part, lse_part, s)
-                  : launch<D, false, true, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
-                                                   o_part, lse_part, s);
+    return causal ? launch<D, 4, true, true, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
+                                                     o_part, lse_part, s)
+                  : launch<D, 4, false, true, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt,
+                                                      splits, o_part, lse_part, s);
   }
-  return causal ? launch<D, true, false, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
-                                                 o_part, lse_part, s)
-                : launch<D, false, false, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
-                                                  o_part, lse_part, s);
+  // Eight wavefronts for rows without a causal diagonal or with many key
+  // tiles per diagonal (the crossover measured at N = 4096).
+  if constexpr (D == 128 && !kSplit) {
+    if (!causal) {
+      return launch<D, 8, false, false, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
+                                                o_part, lse_part, s);
+    }
+    if (N >= 4096) {
+      return launch<D, 8, true, false, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
+                                               o_part, lse_part, s);
+    }
+  }
+  return causal ? launch<D, 4, true, false, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
+                                                    o_part, lse_part, s)
+                : launch<D, 4, false, false, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt,
+                                                     splits, o_part, lse_part, s);
 }
 
 AttnOptions make_options(int N, float scale, const int32_t* kv_len, const float* bias,

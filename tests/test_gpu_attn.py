@@ -65,6 +65,9 @@ ODD = [
     (1, 2, 255, 64), (1, 1, 1000, 64),
     (1, 1, 1, 128), (1, 2, 17, 128), (2, 1, 64, 128), (1, 3, 100, 128), (1, 1, 129, 128),
     (1, 2, 255, 128), (1, 1, 1000, 128), (1, 1, 2049, 128),
+    # Causal rows this long take the 8-wavefront workgroups (as unmasked
+    # rows of any length at D = 128 do); a ragged tail past 4096.
+    (1, 2, 4100, 128),
 ]
 
 
