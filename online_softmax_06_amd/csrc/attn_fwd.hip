@@ -314,7 +314,7 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
     va[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   f32x16 sn = f32x16{};
-  if constexpr (kNext) {
+  if constexpr (kNext && !kMask) {
     read_k(0);
     read_k(1);
   }
@@ -323,15 +323,15 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
   float ps0 = 0.0f, ps1 = 0.0f;  // this lane's half of the sub-tile's row sum
   if constexpr (kMask) {
     // Masked sub-tiles (the last key tiles): the row max decides the new
-    // reference before any exponential.
+    // reference before any exponential.  Here the vector work of phase 1
+    // runs alone and the next scores are formed in phase 2, beside the PV
+    // products, once P is packed: with the float32 P, the next scores and
+    // their K operands all live at once, the extra registers of the masking
+    // push the kernel past 256 VGPRs.
     float m_new = 0.0f, ref = 0.0f;
     constexpr int kExpRegions = kDC - 1;
 #pragma unroll
     for (int c = 0; c < kDC; ++c) {
-      if constexpr (kNext) {
-        if (c + 2 < kDC) read_k(c + 2);
-        sn = mfma32(ka[c % 3], st.qreg[c], sn);
-      }
       // One global->LDS copy instruction per region (regions 1..): spread
       // out, they do not queue up behind the other waves' copies.
       if (c > 0) copy(c - 1);
@@ -358,8 +358,12 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
         const int lo = (c - 1) * 16 / kExpRegions, hi = c * 16 / kExpRegions;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          if (i >= lo && i < hi) p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref));
+          if (i >= lo && i < hi) {
+            p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref));
+            if (i & 1) ps1 += p[i]; else ps0 += p[i];
+          }
         }
+        asm volatile("" : "+v"(ps0), "+v"(ps1));
       }
       if (c == kDC - 1) {
         read_v(0);
@@ -452,28 +456,20 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
                            pack_bf16x2(p[o + 4], p[o + 5]), pack_bf16x2(p[o + 6], p[o + 7])));
   };
   pack_p(0);
-  if constexpr (kMask) {
-    ps0 = p[0];
-    ps1 = p[1];
+  static_assert(kPV == kDC, "one next-score product per PV product");
+  if constexpr (kMask && kNext) {
+    read_k(0);
+    read_k(1);
   }
-  constexpr int kAdds = 16 / kPV;  // scores summed per region (masked sub-tiles)
 #pragma unroll
   for (int i = 0; i < kPV; ++i) {
     const int kc2 = i / kDB, b = i % kDB;
     if (i + 2 < kPV) read_v(i + 2);
     if (i == 0) pack_p(1);
     st.oacc[b] = mfma32(va[i % 3], pb[kc2], st.oacc[b]);
-    if constexpr (kMask) {
-#pragma unroll
-      for (int t = 0; t < kAdds; ++t) {
-        const int e = i * kAdds + t;
-        if (e < 2) continue;
-        if (t & 1) ps1 += p[e]; else ps0 += p[e];
-      }
-      // Keep each region's share of the row sum in the region: otherwise the
-      // compiler defers the sums of several sub-tiles to the end of the loop
-      // body, where they run without products beside them and keep P live.
-      asm volatile("" : "+v"(ps0), "+v"(ps1));
+    if constexpr (kMask && kNext) {
+      if (i + 2 < kDC) read_k(i + 2);
+      sn = mfma32(ka[i % 3], st.qreg[i], sn);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
