@@ -317,8 +317,8 @@ hipError_t launch_resident(const void* in, void* out, int64_t rows, int cols,
 }
 
 // Pick the smallest resident configuration that holds `nvec` vectors per row:
-// one wavefront per row for short rows, 256 threads for medium rows, 1024
-// threads for long rows, at most 64 values per lane (so that 1024-thread
+// one wavefront per row for short rows, 128 or 256 threads for medium rows,
+// 1024 threads for long rows, at most 64 values per lane (so that 1024-thread
 // workgroups fit in 128 VGPRs); otherwise the looping kernel.
 template <typename E, int VEC>
 hipError_t dispatch(const void* in, void* out, int64_t rows, int cols, const RowOptions& opt,
@@ -330,6 +330,12 @@ hipError_t dispatch(const void* in, void* out, int64_t rows, int cols, const Row
   if (nvec <= 64 * 4) return launch_resident<E, VEC, 4, 64>(in, out, rows, cols, opt, s);
   if constexpr (kMaxNV >= 8) {
     if (nvec <= 64 * 8) return launch_resident<E, VEC, 8, 64>(in, out, rows, cols, opt, s);
+  }
+  if constexpr (VEC == 4) {
+    // Float32 rows of 4097..8192 values: two rows per workgroup, 128 threads
+    // and 64 values per lane (measured 4% above one row per 256 threads).
+    if (nvec > 256 * 4 && nvec <= 128 * 16)
+      return launch_resident<E, VEC, 16, 128>(in, out, rows, cols, opt, s);
   }
   if (nvec <= 256 * 4) return launch_resident<E, VEC, 4, 256>(in, out, rows, cols, opt, s);
   if (nvec <= 256 * kMaxNV / 2 && kMaxNV / 2 > 4)
