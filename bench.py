@@ -18,6 +18,11 @@ holds each kernel against its roofline; ``roofline`` repeats the kernel that
 takes the largest share of a step.  Kernel times come from HIP events recorded
 on the launch stream around every launch of the timed steps.
 
+Context fields: ``copy_ceiling`` is a device-to-device ``hipMemcpyAsync`` of
+the float32 softmax bytes (the practical streaming ceiling the softmax runs
+are compared with) and ``sclk_mhz`` the engine clock read from the driver's
+``pp_dpm_sclk`` while the timed steps run (null where the file is absent).
+
 ``--only`` runs a single unit (for profiler runs); ``--copy`` times a plain
 device copy of the float32 softmax bytes (the counter calibration kernel).
 """
@@ -29,6 +34,7 @@ import math
 import os
 import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -192,6 +198,86 @@ def cpu_baseline(torch, osm_inputs, budget_s):
     }
 
 
+class SclkSampler:
+    """Reads the current engine clock (the level marked '*' in the driver's
+    pp_dpm_sclk) every few milliseconds on a side thread."""
+
+    def __init__(self):
+        import glob
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    def _read(self):
+        for p in self.paths:
+            try:
+                for line in open(p):
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+                        if m:
+                            return int(m.group(1))
+            except OSError:
+                pass
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(0.005)
+
+    def start(self):
+        if self.paths:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self):
+        # Samples taken while the GPU was busy (the idle level is far below).
+        busy = [v for v in self.samples if v >= 1000]
+        if not busy:
+            return None
+        busy.sort()
+        return {"median": busy[len(busy) // 2], "min": busy[0], "max": busy[-1],
+                "samples": len(busy), "source": "pp_dpm_sclk during the timed steps"}
+
+
+def copy_ceiling(torch, osm_inputs, steps=20):
+    """Device-to-device hipMemcpyAsync of the float32 softmax bytes."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_void_p]
+    x = osm_inputs.softmax_large(device="cuda")
+    y = torch.empty_like(x)
+    nbytes = x.numel() * 4
+    st = torch.cuda.current_stream()
+    def one():
+        # 3 = hipMemcpyDeviceToDevice
+        if hip.hipMemcpyAsync(y.data_ptr(), x.data_ptr(), nbytes, 3, st.cuda_stream) != 0:
+            raise RuntimeError("hipMemcpyAsync failed")
+    for _ in range(3):
+        one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        one()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del x, y
+    return {"GB/s": round(2 * nbytes / ms / 1e6, 1), "ms": round(ms, 5),
+            "frac_of_hbm_peak": round(2 * nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "method": "hipMemcpyAsync device-to-device, 1 GiB read + 1 GiB written"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +338,7 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    sclk = SclkSampler()
     t_start.record(stream)
     for s in range(args.steps):
         for i, u in enumerate(units):
@@ -259,7 +346,9 @@ def main():
             u.launch()
             marks[s][i][1].record(stream)
     t_end.record(stream)
+    sclk.start()  # samples while the queued steps run
     torch.cuda.synchronize()
+    sclk.stop()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps if units else 0.0
     for s in range(args.steps):
         for i, u in enumerate(units):
@@ -340,6 +429,12 @@ def main():
             "value": bw[0]["achieved"], "unit": "TFLOP/s", "frac_of_bf16_peak": bw[0]["frac"],
             "avg_ms": bw[0]["avg_ms"], "in_step": False,
             "flop_convention": "10*D per unmasked (query, key) pair (five products)"}
+    result["sclk_mhz"] = sclk.summary()
+    if args.only is None:
+        cc = copy_ceiling(torch, osm_inputs)
+        if sm:
+            cc["softmax_frac_of_copy"] = round(value / cc["GB/s"], 4)
+        result["copy_ceiling"] = cc
     if not args.no_cpu_baseline and args.only is None:
         result["cpu_baseline"] = cpu_baseline(torch, osm_inputs, args.cpu_budget)
         result["cpu_baseline"]["host_cpus"] = len(os.sched_getaffinity(0))
