@@ -46,6 +46,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "osm_device.h"
 #include "osm_internal.h"
 
@@ -837,19 +839,20 @@ __global__ __launch_bounds__(256) void attn_split_merge_kernel(const float* __re
   if (dq == 0) lse[row] = L > 0.0f ? M + log2_hw(L) * kLn2 : kNegInf;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; relaxed atomics,
+// since calls from several host threads may fill the same entry).
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int D, int kW, bool kCausal, bool kBias, bool kSplit>
