@@ -75,8 +75,10 @@ SHAPES = [(1, 1), (3, 3), (5, 17), (7, 100), (4, 1000), (2, 1024), (3, 2049), (3
           (2, 8192), (2, 12289), (2, 16384), (1, 40000), (2, 65536), (1, 70001), (1, 150000),
           # Float32 rows of 4097..8192 values run two to a workgroup: odd row
           # counts leave the last workgroup's second row empty, and ragged
-          # widths leave lanes without a vector.
-          (3, 4100), (3, 5000), (5, 8188)]
+          # widths leave lanes without a vector.  Bfloat16 rows of that
+          # length run on 512 threads: 4104 and 8184 are just past and just
+          # short of the edges of that range.
+          (3, 4100), (3, 5000), (5, 8188), (3, 4104), (1, 8184)]
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
