@@ -266,14 +266,16 @@ struct WaveState {
 
 // One 32-key sub-tile s (keys [32 s, 32 s + 32), the half kKb of its 64-key
 // tile) for one wavefront, in two phases.
-//   Phase 1: the scores of sub-tile s + 1 (with kNext) are formed on the
-//            matrix core from `kslot_next` while the vector unit masks the
-//            current scores, finds their row max and exponentiates them;
-//            neither depends on the other, so both units work side by side.
+//   Phase 1: the vector unit exponentiates the current scores and sums them;
+//            on unmasked sub-tiles the scores of sub-tile s + 1 (with kNext)
+//            are formed on the matrix core from `kslot_next` at the same
+//            time (neither depends on the other, so both units work side by
+//            side); masked sub-tiles first hide keys and take the row max.
 //   Phase 2: O is rescaled by alpha (only when some lane needs it), then
 //            O^T += V^T P^T on the two 16-key slices of this sub-tile, fed by
 //            transposed V reads from `vtile`, while the vector unit packs P to
-//            bfloat16 and sums it.
+//            bfloat16; on masked sub-tiles the next scores are formed here,
+//            beside the PV products.
 // Each phase is a sequence of short regions (one or two products, the LDS
 // reads they need two regions later, a share of the vector work) fenced by
 // sched_barrier, so the compiler keeps this interleaving.  `copy(i)` issues
@@ -447,7 +449,7 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
     }
   }
 
-  // Phase 2 (A6): O^T += V^T P^T (and, on masked sub-tiles, the row sum).
+  // Phase 2 (A6): O^T += V^T P^T (and, on masked sub-tiles, the next scores).
   // P in the B-operand layout: slice kc2 holds scores kc2 * 8 + 0..7, i.e.
   // keys 16 kc2 + {0..3, 8..11} + 4 half, the order the V reads follow.
   bf16x8 pb[2];
