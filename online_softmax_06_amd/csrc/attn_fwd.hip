@@ -409,7 +409,12 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
       for (int t = 0; t < kPer; ++t) {
         const int i = c * kPer + t;
         p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref));
-        if (t & 1) ps1 += p[i]; else ps0 += p[i];
+        // The first two values start the two sums (no add of 0).
+        if (i < 2) {
+          if (t & 1) ps1 = p[i]; else ps0 = p[i];
+        } else {
+          if (t & 1) ps1 += p[i]; else ps0 += p[i];
+        }
       }
       // Keep this region's exponentials and sums in the region.
       asm volatile("" : "+v"(ps0), "+v"(ps1));
@@ -422,8 +427,10 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
     asm volatile("" ::"v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]),
                  "v"(p[6]), "v"(p[7]), "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]),
                  "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
-    const bool settled = ps0 + ps1 <= 0x1p64f && st.m_run != kNegInf;
-    if (__builtin_amdgcn_ballot_w64(!settled) != 0) {
+    // One ballot per condition: each compare then feeds the branch directly.
+    const float ps = ps0 + ps1;
+    if ((__builtin_amdgcn_ballot_w64(!(ps <= 0x1p64f)) |
+         __builtin_amdgcn_ballot_w64(st.m_run == kNegInf)) != 0) {
       // Rare: the row max, a new reference (raised only past kLag), the
       // rescale of O and l, and P again.
       asm volatile("");
