@@ -409,15 +409,16 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
       for (int t = 0; t < kPer; ++t) {
         const int i = c * kPer + t;
         p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref));
-        // The first two values start the two sums (no add of 0).
-        if (i < 2) {
-          if (t & 1) ps1 = p[i]; else ps0 = p[i];
-        } else {
+        // The sums start as p0 + p2 and p1 + p3: no add of 0 and no copy.
+        if (i == 2) ps0 = p[0] + p[2];
+        if (i == 3) ps1 = p[1] + p[3];
+        if (i >= 4) {
           if (t & 1) ps1 += p[i]; else ps0 += p[i];
         }
       }
-      // Keep this region's exponentials and sums in the region.
-      asm volatile("" : "+v"(ps0), "+v"(ps1));
+      // Keep this region's exponentials and sums in the region (once both
+      // sums exist).
+      if (c * kPer + kPer > 3) asm volatile("" : "+v"(ps0), "+v"(ps1));
       if (c == kDC - 1) {
         read_v(0);
         read_v(1);
