@@ -610,25 +610,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   };
   using Masked = std::integral_constant<bool, true>;
   using Plain = std::integral_constant<bool, false>;
-  // Masked tiles: those crossing the causal diagonal or the end of the keys.
-  const int t_plain_end = min(kCausal ? qt * (kBlk / kTile) : nkt, kvlen / kTile);
-  auto run = [&](const char* kbuf, const char* vbuf, int t) __attribute__((always_inline)) {
-    if (t >= t_plain_end) compute(Masked{}, kbuf, vbuf, t);
-    else compute(Plain{}, kbuf, vbuf, t);
+  using Stage0 = std::integral_constant<int, 0>;
+  using Stage1 = std::integral_constant<int, 1>;
+  // Tile t sits in stage t & 1.  A step waits for its tile, starts the copy
+  // of the next one into the other stage and computes.
+  auto step = [&](auto masked, auto stage, int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if constexpr (decltype(stage)::value == 0) {
+      if (t + 1 < t_end) issue(ks1, vs1, t + 1);
+      compute(masked, ks0, vs0, t);
+    } else {
+      if (t + 1 < t_end) issue(ks0, vs0, t + 1);
+      compute(masked, ks1, vs1, t);
+    }
   };
+  // Masked tiles, those crossing the causal diagonal or the end of the keys,
+  // all come after the plain ones.  Each kind runs in a loop of its own, so
+  // the accumulators keep one register assignment through every iteration.
+  const int t_plain_end = min(min(kCausal ? qt * (kBlk / kTile) : nkt, kvlen / kTile), t_end);
 
   if (t_end > 0) issue(ks0, vs0, 0);
-  for (int t = 0; t < t_end; t += 2) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 1 < t_end) issue(ks1, vs1, t + 1);
-    run(ks0, vs0, t);
-    if (t + 1 >= t_end) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 2 < t_end) issue(ks0, vs0, t + 2);
-    run(ks1, vs1, t + 1);
+  int t = 0;
+  for (; t + 1 < t_plain_end; t += 2) {
+    step(Plain{}, Stage0{}, t);
+    step(Plain{}, Stage1{}, t + 1);
   }
+  if (t < t_plain_end) {
+    step(Plain{}, Stage0{}, t);
+    ++t;
+    if (t < t_end) step(Masked{}, Stage1{}, t++);
+  }
+  for (; t + 1 < t_end; t += 2) {
+    step(Masked{}, Stage0{}, t);
+    step(Masked{}, Stage1{}, t + 1);
+  }
+  if (t < t_end) step(Masked{}, Stage0{}, t);
 
   // dQ^T: lane = query row, register i of block b = dim 32 b + 8 (i / 4) +
   // 4 half + i % 4.
