@@ -14,20 +14,21 @@
 // with Delta_i computed as the row dot product dO_i . O_i (equal to the sum
 // above because O_i = sum_j P_ij V_j), so it costs one pass over O and dO.
 //
-// Three launches, no atomics (the result is deterministic):
-//   prep  Delta and LSE * log2 e per query row into a padded workspace
-//         (padding rows get Delta = 0 and +inf, so their P is exactly 0);
+// Two launches, no atomics (the result is deterministic):
+//   dq    a workgroup owns 128 query rows (32 per wavefront), computes their
+//         Delta and LSE * log2 e from its own loads of O, dO and LSE and
+//         writes them to a padded workspace for dkdv (padding rows get
+//         Delta = 0 and +inf, so their P is exactly 0), keeps Q, dO, Delta,
+//         LSE and the dQ^T accumulator in registers and streams the 64-key
+//         tiles of K and V: S^T = K Q^T, dP^T = V dO^T, P, dS, then
+//         dQ^T += K^T dS^T;
 //   dkdv  a workgroup owns 128 keys (32 per wavefront), keeps their K rows
 //         in LDS, their V fragments and the dK^T, dV^T accumulators in
 //         registers, and streams 32-row tiles of Q and dO (plus their Delta
 //         and LSE) through LDS: per tile S = Q K^T, dP = dO V^T, P, dS, then
-//         dV^T += dO^T P and dK^T += Q^T dS (two workgroups per CU);
-//   dq    a workgroup owns 128 query rows (32 per wavefront), keeps Q, dO,
-//         Delta, LSE and the dQ^T accumulator in registers and streams the
-//         64-key tiles of K and V: S^T = K Q^T, dP^T = V dO^T, P, dS, then
-//         dQ^T += K^T dS^T.
-// The second kernel repeats two of the first kernel's products (the scores
-// and dP) instead of adding partial dQ into HBM with atomics.
+//         dV^T += dO^T P and dK^T += Q^T dS (two workgroups per CU).
+// dkdv repeats two of the dq kernel's products (the scores and dP) instead
+// of adding partial dQ into HBM with atomics.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64).  A product whose
 // output has lanes = the index kept by the wavefront and registers = the
@@ -284,45 +285,6 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& a, int i0, f
 }
 
 // ---------------------------------------------------------------------------
-// prep: Delta_i = dO_i . O_i and LSE_i * log2 e per query row, over the padded
-// range [0, Np) of every head.  D / 8 lanes share a row, 8 elements each.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
-    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ delta, float* __restrict__ lse2, int BH, int N, int Np) {
-  constexpr int kLanes = D / 8;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = t / kLanes;  // over BH * Np
-  const int part = (int)(t % kLanes);
-  const int64_t bh = row / Np;
-  const int i = (int)(row % Np);
-  float acc = 0.0f;
-  if (bh < BH && i < N) {
-    const int64_t e = (bh * N + i) * D + part * 8;
-    const uint4 a = *reinterpret_cast<const uint4*>(o + e);
-    const uint4 g = *reinterpret_cast<const uint4*>(dout + e);
-    acc = bf16_lo(a.x) * bf16_lo(g.x);
-    acc = __builtin_fmaf(bf16_hi(a.x), bf16_hi(g.x), acc);
-    acc = __builtin_fmaf(bf16_lo(a.y), bf16_lo(g.y), acc);
-    acc = __builtin_fmaf(bf16_hi(a.y), bf16_hi(g.y), acc);
-    acc = __builtin_fmaf(bf16_lo(a.z), bf16_lo(g.z), acc);
-    acc = __builtin_fmaf(bf16_hi(a.z), bf16_hi(g.z), acc);
-    acc = __builtin_fmaf(bf16_lo(a.w), bf16_lo(g.w), acc);
-    acc = __builtin_fmaf(bf16_hi(a.w), bf16_hi(g.w), acc);
-  }
-#pragma unroll
-  for (int m = 1; m < kLanes; m <<= 1) acc += __shfl_xor(acc, m, kLanes);
-  if (part == 0 && bh < BH) {
-    delta[row] = acc;
-    const float l = i < N ? lse[bh * N + i] : kNegInf;
-    // A row without a visible key (LSE = -inf) and a padding row get +inf:
-    // every P of the row is then 2^-inf = 0.
-    lse2[row] = l == kNegInf ? __builtin_inff() : l * kLog2e;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // dkdv: dK and dV of 128 keys per workgroup (32 per wavefront), two
 // workgroups per CU.  The block's K rows stay in LDS (B operand of the
 // scores, read like a streamed tile), its V fragments in registers, and the
@@ -528,10 +490,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
 template <int D, bool kCausal>
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dq,
-    int BH, int H, int N, int Np, const int32_t* __restrict__ kv_len, float scale,
-    float scale_log2) {
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ lse2,
+    float* __restrict__ delta, uint16_t* __restrict__ dq, int BH, int H, int N, int Np,
+    const int32_t* __restrict__ kv_len, float scale, float scale_log2) {
   using G = Geo<D>;
   constexpr int kDC = G::kDC, kDB = G::kDB;
   __shared__ __attribute__((aligned(1024))) char ks0[G::kBytes];
@@ -552,16 +514,38 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   const int qrow = qw + col;             // this lane's query row (< Np)
 
   // B operands of S^T = K Q^T and dP^T = V dO^T: row `qrow`, dims
-  // 16 c + 8 half + 0..7.
+  // 16 c + 8 half + 0..7.  The same dims of O give this lane's half of
+  // Delta = dO . O; the lane 32 apart holds the other half.
   bf16x8 qreg[kDC], oreg[kDC];
+  float dl = 0.0f;
 #pragma unroll
   for (int c = 0; c < kDC; ++c) {
     const int64_t e = head + (int64_t)qrow * D + c * 16 + half * 8;
     qreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(q + e) : bf16x8{};
     oreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(dout + e) : bf16x8{};
+    if (qrow < N) {
+      const uint4 a = *reinterpret_cast<const uint4*>(o + e);
+      const uint4 g = __builtin_bit_cast(uint4, oreg[c]);
+      dl = __builtin_fmaf(bf16_lo(a.x), bf16_lo(g.x), dl);
+      dl = __builtin_fmaf(bf16_hi(a.x), bf16_hi(g.x), dl);
+      dl = __builtin_fmaf(bf16_lo(a.y), bf16_lo(g.y), dl);
+      dl = __builtin_fmaf(bf16_hi(a.y), bf16_hi(g.y), dl);
+      dl = __builtin_fmaf(bf16_lo(a.z), bf16_lo(g.z), dl);
+      dl = __builtin_fmaf(bf16_hi(a.z), bf16_hi(g.z), dl);
+      dl = __builtin_fmaf(bf16_lo(a.w), bf16_lo(g.w), dl);
+      dl = __builtin_fmaf(bf16_hi(a.w), bf16_hi(g.w), dl);
+    }
   }
-  const float l2 = lse2[(int64_t)bh * Np + qrow];
-  const float dl = delta[(int64_t)bh * Np + qrow];
+  dl += __shfl_xor(dl, 32);
+  // A row without a visible key (LSE = -inf) and a padding row get +inf:
+  // every P of the row is then 2^-inf = 0.
+  const float lv = qrow < N ? lse[(int64_t)bh * N + qrow] : kNegInf;
+  const float l2 = lv == kNegInf ? __builtin_inff() : lv * kLog2e;
+  // The grid covers the padded rows [0, Np) of every head exactly once.
+  if (half == 0) {
+    delta[(int64_t)bh * Np + qrow] = dl;
+    lse2[(int64_t)bh * Np + qrow] = l2;
+  }
   f32x16 dqa[kDB];
 #pragma unroll
   for (int b = 0; b < kDB; ++b) dqa[b] = f32x16{};
@@ -671,16 +655,16 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   const auto* k16 = static_cast<const uint16_t*>(k);
   const auto* v16 = static_cast<const uint16_t*>(v);
   const auto* g16 = static_cast<const uint16_t*>(dout);
-  const int64_t prep_threads = (int64_t)BH * Np * (D / 8);
-  attn_bwd_prep_kernel<D><<<dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, stream>>>(
-      static_cast<const uint16_t*>(o), g16, lse, delta, lse2, BH, N, Np);
+  // Np == number of dQ workgroups per head * kBlk: the dQ kernel writes
+  // Delta and LSE * log2 e for every padded row, which dK/dV then reads.
+  static_assert(kPad == kBlk, "one dQ workgroup per padded block of rows");
   const unsigned blocks = (unsigned)((int64_t)BH * ((N + kBlk - 1) / kBlk));
+  attn_bwd_dq_kernel<D, kCausal><<<dim3(blocks), dim3(kThreads), 0, stream>>>(
+      q16, k16, v16, static_cast<const uint16_t*>(o), g16, lse, lse2, delta,
+      static_cast<uint16_t*>(dq), BH, H, N, Np, kv_len, scale, scale_log2);
   attn_bwd_dkdv_kernel<D, kCausal><<<dim3(blocks), dim3(kThreads), 0, stream>>>(
       q16, k16, v16, g16, lse2, delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), BH,
       H, N, Np, kv_len, scale, scale_log2);
-  attn_bwd_dq_kernel<D, kCausal><<<dim3(blocks), dim3(kThreads), 0, stream>>>(
-      q16, k16, v16, g16, lse2, delta, static_cast<uint16_t*>(dq), BH, H, N, Np, kv_len, scale,
-      scale_log2);
   return hipGetLastError();
 }
 

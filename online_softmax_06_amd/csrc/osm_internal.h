@@ -43,7 +43,7 @@ hipError_t attn_fwd_split_launch(const void* q, const void* k, const void* v, vo
 
 // Attention backward: workspace bytes (Delta and LSE * log2 e per query row,
 // float32, rows padded to a multiple of 128 per head), and the launch of the
-// three kernels (prep, dK/dV, dQ).  D must be 64 or 128; kv_len (nullable,
+// two kernels (dQ, which also fills the workspace, then dK/dV).  D must be 64 or 128; kv_len (nullable,
 // int32 [B]) limits the keys of each batch as in the forward.
 int64_t attn_bwd_workspace(int B, int H, int N);
 hipError_t attn_bwd_launch(const void* q, const void* k, const void* v, const void* o,
