@@ -278,12 +278,6 @@ __device__ __forceinline__ void block_of(int L, int per_head, int BH, int& bh, i
   }
 }
 
-// Store 4 consecutive floats times `mul` as bfloat16 (8 bytes).
-__device__ __forceinline__ void store4(uint16_t* dst, const f32x16& a, int i0, float mul) {
-  *reinterpret_cast<uint2*>(dst) =
-      make_uint2(pack_bf16x2(a[i0] * mul, a[i0 + 1] * mul), pack_bf16x2(a[i0 + 2] * mul, a[i0 + 3] * mul));
-}
-
 // ---------------------------------------------------------------------------
 // dkdv: dK and dV of 128 keys per workgroup (32 per wavefront), two
 // workgroups per CU.  The block's K rows stay in LDS (B operand of the
@@ -474,12 +468,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
     uint16_t* dvr = dv + head + (int64_t)key * D;
 #pragma unroll
     for (int b = 0; b < kDB; ++b) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = b * 32 + 8 * j + 4 * half;
-        store4(dkr + d, dka[b], 4 * j, scale);
-        store4(dvr + d, dva[b], 4 * j, 1.0f);
-      }
+      store_block_bf16(dkr + b * 32, dka[b], half, scale);
+      store_block_bf16(dvr + b * 32, dva[b], half, 1.0f);
     }
   }
 }
@@ -636,10 +626,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   if (qrow < N) {
     uint16_t* dqr = dq + head + (int64_t)qrow * D;
 #pragma unroll
-    for (int b = 0; b < kDB; ++b) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) store4(dqr + b * 32 + 8 * j + 4 * half, dqa[b], 4 * j, scale);
-    }
+    for (int b = 0; b < kDB; ++b) store_block_bf16(dqr + b * 32, dqa[b], half, scale);
   }
 }
 

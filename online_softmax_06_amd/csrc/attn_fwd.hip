@@ -792,19 +792,11 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads), (Shape<D, kW>::kPerCU)) v
         }
         if (half == 0) lse_part[prow] = lse_val;
       } else {
+        // O^T block bb holds dims bb*32 + 8 (i / 4) + 4 half + i % 4; the
+        // stores trade columns with the partner lane first (16 bytes per lane).
         uint16_t* orow = o + head_off + (int64_t)qrow * D;
 #pragma unroll
-        for (int bb = 0; bb < kDB; ++bb) {
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            // O^T rows bb*32 + gq*8 + half*4 + (0..3): four consecutive dims.
-            const f32x16& oa = st.oacc[bb];
-            uint2 w;
-            w.x = pack_bf16x2(oa[gq * 4 + 0] * inv, oa[gq * 4 + 1] * inv);
-            w.y = pack_bf16x2(oa[gq * 4 + 2] * inv, oa[gq * 4 + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + bb * 32 + gq * 8 + half * 4) = w;
-          }
-        }
+        for (int bb = 0; bb < kDB; ++bb) store_block_bf16(orow + bb * 32, st.oacc[bb], half, inv);
         if (half == 0) lse[(int64_t)bh * N + qrow] = lse_val;
       }
     }

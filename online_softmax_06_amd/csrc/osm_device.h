@@ -109,4 +109,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
+// Stores one 32-column block of a transposed 32x32 matrix-core accumulator
+// (lane = row, shared with the partner lane ^ 32; register i = column
+// 8 (i / 4) + 4 half + i % 4, half = lane / 32) times `mul` as bfloat16 to
+// row[0..31].  One v_permlane32_swap per register pair first trades four of
+// this lane's columns for four of the partner's, so that every lane holds 8
+// consecutive columns (16 p + 8 half + 0..7 in registers 8 p .. 8 p + 7) and
+// writes them with one 16-byte store: half the store instructions of 8-byte
+// stores, and each covers 32 contiguous bytes of every row.  Both lanes of a
+// row must be active.
+template <typename V>
+__device__ __forceinline__ void store_block_bf16(uint16_t* row, V a, int half, float mul) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[8 * p + t]),
+                                                      __float_as_uint(a[8 * p + 4 + t]), false,
+                                                      false);
+      a[8 * p + t] = __uint_as_float(r[0]);
+      a[8 * p + 4 + t] = __uint_as_float(r[1]);
+    }
+    uint4 w;
+    w.x = pack_bf16x2(a[8 * p + 0] * mul, a[8 * p + 1] * mul);
+    w.y = pack_bf16x2(a[8 * p + 2] * mul, a[8 * p + 3] * mul);
+    w.z = pack_bf16x2(a[8 * p + 4] * mul, a[8 * p + 5] * mul);
+    w.w = pack_bf16x2(a[8 * p + 6] * mul, a[8 * p + 7] * mul);
+    *reinterpret_cast<uint4*>(row + 16 * p + 8 * half) = w;
+  }
+}
+
 }  // namespace osm
