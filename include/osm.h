@@ -249,7 +249,7 @@ int64_t osm_attn_fwd_split_workspace(int B, int H, int N, int D, int splits);
  *               osm_attn_bwd_workspace(B, H, N, D) bytes; its content on
  *               entry does not matter.  Calls that share a workspace must be
  *               ordered (same stream).
- *   stream      hipStream_t to enqueue on (three kernels, in order).
+ *   stream      hipStream_t to enqueue on (two kernels, in order).
  *
  * The result does not depend on the launch (no atomics): equal inputs give
  * bitwise equal gradients.  Returns as osm_attn_fwd, plus OSM_ERR_INVALID_ARG
