@@ -17,16 +17,18 @@
 // Two launches, no atomics (the result is deterministic):
 //   dq    a workgroup owns 128 query rows (32 per wavefront), computes their
 //         Delta and LSE * log2 e from its own loads of O, dO and LSE and
-//         writes them to a padded workspace for dkdv (padding rows get
-//         Delta = 0 and +inf, so their P is exactly 0), keeps Q, dO, Delta,
-//         LSE and the dQ^T accumulator in registers and streams the 64-key
-//         tiles of K and V: S^T = K Q^T, dP^T = V dO^T, P, dS, then
-//         dQ^T += K^T dS^T;
+//         writes -Delta and LSE * log2 e to a padded workspace for dkdv
+//         (padding rows get 0 and +inf, so their P is exactly 0), keeps Q,
+//         dO, Delta, LSE and the dQ^T accumulator in registers and streams
+//         the 64-key tiles of K and V: S^T = K Q^T, dP^T = V dO^T, P, dS,
+//         then dQ^T += K^T dS^T;
 //   dkdv  a workgroup owns 128 keys (32 per wavefront), keeps their K rows
 //         in LDS, their V fragments and the dK^T, dV^T accumulators in
-//         registers, and streams 32-row tiles of Q and dO (plus their Delta
+//         registers, and streams 32-row tiles of Q and dO (plus their -Delta
 //         and LSE) through LDS: per tile S = Q K^T, dP = dO V^T, P, dS, then
 //         dV^T += dO^T P and dK^T += Q^T dS (two workgroups per CU).
+// Both kernels start the dP accumulator from -Delta instead of zero, so the
+// products leave dP - Delta and dS = P * dP costs one multiply.
 // dkdv repeats two of the dq kernel's products (the scores and dP) instead
 // of adding partial dQ into HBM with atomics.
 //
@@ -204,8 +206,9 @@ __device__ __forceinline__ bf16x8 pack8(const float (&x)[16], int kc2) {
 // Output register i of a 32 x 32 product sits in row rho(i) + 4 half.
 __device__ __forceinline__ constexpr int rho(int i) { return (i >> 2) * 8 + (i & 3); }
 
-// The two first products of a 32-row sub-tile, s1 = A1 B1 and s2 = A2 B2
-// over the kDC slices of the head dimension: A rows [r0, r0 + 32) of the
+// The two first products of a 32-row sub-tile, s1 = A1 B1 and
+// s2 = s2_init + A2 B2 over the kDC slices of the head dimension: A rows
+// [r0, r0 + 32) of the
 // streamed tiles t1 and t2, B in registers.  Each region (fenced by
 // sched_barrier) issues one product of each and the LDS reads of the next
 // slice, so few operands are live at a time.
@@ -214,7 +217,7 @@ __device__ __forceinline__ void first_products(const char* t1, const char* t2,
                                                const ReadOffsets<D>& off, int r0,
                                                const bf16x8 (&b1)[D / 16],
                                                const bf16x8 (&b2)[D / 16], f32x16& s1,
-                                               f32x16& s2) {
+                                               f32x16& s2, const f32x16& s2_init) {
   constexpr int kDC = D / 16, kBuf = kAhead + 1;
   bf16x8 a1[kBuf], a2[kBuf];
 #pragma unroll
@@ -223,7 +226,7 @@ __device__ __forceinline__ void first_products(const char* t1, const char* t2,
     a2[c] = read_row<D>(t2, off, c, r0);
   }
   s1 = f32x16{};
-  s2 = f32x16{};
+  s2 = s2_init;
 #pragma unroll
   for (int c = 0; c < kDC; ++c) {
     if (c + kAhead < kDC) {
@@ -369,7 +372,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
     // row of the tile (causal: all rows before the keys; or all keys past
     // the key length).
     if (kMasked && ((kCausal && kw > qbase + 31) || kw >= kvlen)) return;
-    f32x16 sc = f32x16{}, dp = f32x16{};
+    // dP starts from -Delta of its rows (register i: row rho(i) + 4 half, four
+    // rows per 16-byte read), so the products leave dP - Delta.
+    f32x16 sc = f32x16{}, dp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(eb + 8 * j + 4 * half);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dp[4 * j + r] = e4[r];
+    }
     {
       constexpr int kAhead = 1, kBuf = kAhead + 1;
       bf16x8 a1[kBuf], a2[kBuf], bk[kBuf];
@@ -391,18 +402,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
     // Key `key` is visible from row qbase + 4 half + rho when rho >= lim.
     const int lim = key - qbase - 4 * half;
     // P (into sc) and dS (into dp), four rows at a time: rows 8 j + 4 half +
-    // 0..3, whose LSE and Delta are one 16-byte read each.
+    // 0..3, whose LSE is one 16-byte read.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + 8 * j + 4 * half);
-      const f32x4 e4 = *reinterpret_cast<const f32x4*>(eb + 8 * j + 4 * half);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * j + r;
         float x = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -l4[r]));
         if (kMasked && ((kCausal && rho(i) < lim) || key >= kvlen)) x = 0.0f;
         sc[i] = x;
-        dp[i] = x * (dp[i] - e4[r]);
+        dp[i] = x * dp[i];
       }
     }
     float p[16], ds[16];
@@ -533,9 +543,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   const float l2 = lv == kNegInf ? __builtin_inff() : lv * kLog2e;
   // The grid covers the padded rows [0, Np) of every head exactly once.
   if (half == 0) {
-    delta[(int64_t)bh * Np + qrow] = dl;
+    delta[(int64_t)bh * Np + qrow] = -dl;
     lse2[(int64_t)bh * Np + qrow] = l2;
   }
+  // dP^T starts from -Delta, so its products leave dP - Delta.
+  f32x16 ndl;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndl[i] = -dl;
   f32x16 dqa[kDB];
 #pragma unroll
   for (int b = 0; b < kDB; ++b) dqa[b] = f32x16{};
@@ -567,7 +581,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       // Masked tiles: every key of the sub-tile is hidden from this wave.
       if (kMasked && (kbase >= kvlen || (kCausal && kbase > qw + 31))) continue;
       f32x16 sc, dp;
-      first_products<D, 0>(kbuf, vbuf, off, r0, qreg, oreg, sc, dp);
+      first_products<D, 0>(kbuf, vbuf, off, r0, qreg, oreg, sc, dp, ndl);
       // Key kbase + 4 half + rho is visible from this row when rho < lim.
       const int lim = vis_end - kbase - 4 * half;
       float ds[16];
@@ -575,7 +589,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       for (int i = 0; i < 16; ++i) {
         float x = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -l2));
         if (kMasked && rho(i) >= lim) x = 0.0f;
-        ds[i] = x * (dp[i] - dl);
+        ds[i] = x * dp[i];
       }
       const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
       __builtin_amdgcn_sched_barrier(0);
