@@ -770,6 +770,12 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads), (Shape<D, kW>::kPerCU)) v
 #undef OSM_TAIL_TILE
 #undef OSM_MAIN_TILE
 #undef OSM_TILE_COPIES
+    // The last tile's copies (zero fills of slots past the item) land before
+    // this wave reaches the next item's barrier, after which other waves
+    // copy the next item's tiles into the same slots: an early copy can then
+    // not overwrite a later one.  They carry no memory traffic, so this wait
+    // is short.
+    __builtin_amdgcn_s_waitcnt(0);
 
     // A7: O = O / l (deferred division), LSE = ln 2 * (m + log2 l).  The
     // stores are not waited for: the next item's loads go out behind them.
