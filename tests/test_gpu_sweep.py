@@ -53,7 +53,7 @@ def _fwd_case(seed):
     return B, H, N, D, causal, scale, kv_len, bias, splits
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(32))
 def test_forward_sweep(seed):
     B, H, N, D, causal, scale, kv_len, bias_spec, splits = _fwd_case(seed)
     _announce("fwd sweep", seed, dict(B=B, H=H, N=N, D=D, causal=causal, scale=scale,
@@ -73,7 +73,7 @@ def test_forward_sweep(seed):
     _compare_attn(q, k, v, scale, causal, kv, bias, o, lse)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(20))
 def test_backward_sweep(seed):
     r = np.random.default_rng(2000 + seed)
     B, H = int(r.integers(1, 3)), int(r.integers(1, 3))
@@ -101,7 +101,7 @@ def test_backward_sweep(seed):
                         kv_len=None if kv_len is None else kv_len[b])
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_softmax_sweep(seed):
     r = np.random.default_rng(3000 + seed)
     rows = int(r.integers(1, 9))
