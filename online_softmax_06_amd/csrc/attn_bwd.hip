@@ -581,9 +581,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       // Masked tiles: every key of the sub-tile is hidden from this wave.
       if (kMasked && (kbase >= kvlen || (kCausal && kbase > qw + 31))) continue;
       f32x16 sc, dp;
-      // D = 128: operands read one slice ahead; D = 64 reads them in place,
-      // which keeps the kernel at 4 workgroups per CU.
-      first_products<D, D == 128 ? 1 : 0>(kbuf, vbuf, off, r0, qreg, oreg, sc, dp, ndl);
+      // Operands read one slice ahead.
+      first_products<D, 1>(kbuf, vbuf, off, r0, qreg, oreg, sc, dp, ndl);
       // Key kbase + 4 half + rho is visible from this row when rho < lim.
       const int lim = vis_end - kbase - 4 * half;
       float ds[16];
