@@ -23,7 +23,8 @@ Context fields: ``copy_ceiling`` is the fastest of 20 device-to-device
 practical streaming ceiling the softmax runs are compared with) and ``sclk_mhz`` the engine clock read from the driver's
 ``pp_dpm_sclk`` while the timed steps run (null where the file is absent).
 
-``--only`` runs a single unit (for profiler runs); ``--copy`` times a plain
+``--only`` runs a single unit (for profiler runs; ``attn_long``, the B1 H32
+N16384 D128 causal workload, runs only this way); ``--copy`` times a plain
 device copy of the float32 softmax bytes (the counter calibration kernel).
 """
 
@@ -111,6 +112,21 @@ def make_units(torch, osm, osm_inputs, only):
                                                         cfg["causal"], out=o, lse=lse)),
             flops, "mfma", BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
             f"attn_llama13b B{a['B']} H{a['H']} N{a['N']} D{a['D']} causal"))
+    if only == "attn_long":
+        # Profiling only (never part of the default step): the long-context
+        # causal workload, B1 H32 N16384 D128, for its counters.
+        cfg = osm_inputs.attention_config("attn_long", device="cuda")
+        a = cfg["cfg"]
+        o = torch.empty_like(cfg["q"])
+        lse = torch.empty((a["B"], a["H"], a["N"]), dtype=torch.float32, device="cuda")
+        pairs = a["N"] * (a["N"] + 1) // 2 if a["causal"] else a["N"] * a["N"]
+        flops = 4 * a["D"] * pairs * a["B"] * a["H"]
+        units.append(Unit(
+            "attn_long", "attn_fwd_kernel<128, causal> (8 wavefronts)", "attn_fwd.hip",
+            (lambda cfg=cfg, o=o, lse=lse: osm.attn_fwd(cfg["q"], cfg["k"], cfg["v"], cfg["scale"],
+                                                        cfg["causal"], out=o, lse=lse)),
+            flops, "mfma", BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
+            f"attn_long B{a['B']} H{a['H']} N{a['N']} D{a['D']} causal", in_step=False))
     if only in (None, "attn_bwd"):
         cfg = osm_inputs.attention_config("attn_llama13b", device="cuda")
         a = cfg["cfg"]
@@ -287,8 +303,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["softmax_f32", "softmax_bf16", "attn", "attn_bwd"],
-                    default=None)
+    ap.add_argument("--only", choices=["softmax_f32", "softmax_bf16", "attn", "attn_bwd",
+                                       "attn_long"], default=None,
+                    help="time one unit (for profiler runs); attn_long runs only here")
     ap.add_argument("--copy", action="store_true", help="time a plain device copy instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -397,7 +414,8 @@ def main():
         sm_ms = sum(r["avg_ms"] for r in sm)
         value, unit = sm_bytes / (sm_ms * 1e-3) / 1e9, "GB/s"
     else:
-        value, unit = (at or bw)[0]["achieved"], "TFLOP/s"
+        first = (at or bw or rooflines)[0]
+        value, unit = first["achieved"], first["unit"]
 
     result = {
         "metric": METRIC,
