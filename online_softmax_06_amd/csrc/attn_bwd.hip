@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
     const bf16x8 pb[2] = {pack8(p, 0), pack8(p, 1)};
     const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
     __builtin_amdgcn_sched_barrier(0);
-    acc_products<D, true, 1>(gb, qb, off, 0, pb, db, dva, dka);
+    acc_products<D, true, 2>(gb, qb, off, 0, pb, db, dva, dka);
   };
 
   using Masked = std::integral_constant<bool, true>;
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       }
       const bf16x8 db[2] = {pack8(ds, 0), pack8(ds, 1)};
       __builtin_amdgcn_sched_barrier(0);
-      acc_products<D, false, 1>(kbuf, kbuf, off, r0, db, db, dqa, dqa);
+      acc_products<D, false, 2>(kbuf, kbuf, off, r0, db, db, dqa, dqa);
     }
   };
   using Masked = std::integral_constant<bool, true>;
