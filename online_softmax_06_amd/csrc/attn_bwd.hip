@@ -382,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
       for (int r = 0; r < 4; ++r) dp[4 * j + r] = e4[r];
     }
     {
-      constexpr int kAhead = 1, kBuf = kAhead + 1;
+      constexpr int kAhead = 2, kBuf = kAhead + 1;
       bf16x8 a1[kBuf], a2[kBuf], bk[kBuf];
       auto fetch = [&](int c) __attribute__((always_inline)) {
         a1[c % kBuf] = read_row<D>(qb, off, c, 0);
@@ -581,8 +581,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       // Masked tiles: every key of the sub-tile is hidden from this wave.
       if (kMasked && (kbase >= kvlen || (kCausal && kbase > qw + 31))) continue;
       f32x16 sc, dp;
-      // Operands read one slice ahead.
-      first_products<D, 1>(kbuf, vbuf, off, r0, qreg, oreg, sc, dp, ndl);
+      // Operands read two slices ahead.
+      first_products<D, 2>(kbuf, vbuf, off, r0, qreg, oreg, sc, dp, ndl);
       // Key kbase + 4 half + rho is visible from this row when rho < lim.
       const int lim = vis_end - kbase - 4 * half;
       float ds[16];
