@@ -36,7 +36,7 @@ Parity status of each function is stated in its docstring.
 """
 
 from .softmax_ref import masked_softmax_rows_ref, naive_softmax_rows_f32, softmax_rows_ref
-from .online_ref import EMPTY_STATE, all_trees, combine, online_state, tree_reduce
+from .online_ref import EMPTY_STATE, all_trees, combine, online_state, singleton, tree_reduce
 from .attention_ref import attention_head_ref, attention_ref, blocked_attention_row_ref
 from .attention_bwd_ref import (attention_bwd_head_ref, attention_bwd_ref, attention_dq_rows_ref,
                                 attention_probs_head_ref)
@@ -47,6 +47,7 @@ __all__ = [
     "naive_softmax_rows_f32",
     "EMPTY_STATE",
     "combine",
+    "singleton",
     "online_state",
     "tree_reduce",
     "all_trees",

@@ -15,7 +15,8 @@ import random
 import numpy as np
 import pytest
 
-from oracle import EMPTY_STATE, all_trees, combine, online_state, softmax_rows_ref, tree_reduce
+from oracle import (EMPTY_STATE, all_trees, combine, online_state, singleton, softmax_rows_ref,
+                    tree_reduce)
 
 
 def _ref_max_sum(xs):
@@ -121,3 +122,75 @@ def test_chunked_states_combine_to_whole():
             st = combine(st, online_state(p))
         assert _close(st, whole, rel=1e-13)
     assert _close(whole, _ref_max_sum(xs), rel=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# The enumeration the every-tree test relies on.  If all_trees returned too
+# few trees (an off-by-one in its split range gives none at all), the test
+# above would pass without trying the association orders it claims to.
+# ---------------------------------------------------------------------------
+
+CATALAN = [1, 1, 2, 5, 14, 42, 132]  # C(n - 1) binary trees over n ordered leaves
+
+
+def _render(tree):
+    """The parenthesisation a tree stands for, written out by the test."""
+    if isinstance(tree, int):
+        return str(tree)
+    return "(" + _render(tree[0]) + "," + _render(tree[1]) + ")"
+
+
+def _leaves(tree):
+    return [tree] if isinstance(tree, int) else _leaves(tree[0]) + _leaves(tree[1])
+
+
+def _stack_parenthesisations(n):
+    """Every full parenthesisation of leaves 0..n-1, enumerated another way:
+    each run of a stack machine that pushes the leaves in order and, at any
+    point, may pop two entries and push their bracketed pair."""
+    found = set()
+
+    def run(stack, nxt):
+        if nxt == n and len(stack) == 1:
+            found.add(stack[0])
+        if nxt < n:
+            run(stack + [str(nxt)], nxt + 1)
+        if len(stack) >= 2:
+            run(stack[:-2] + ["(" + stack[-2] + "," + stack[-1] + ")"], nxt)
+
+    run([], 0)
+    return found
+
+
+@pytest.mark.parametrize("n", range(1, 8))
+def test_all_trees_is_every_parenthesisation(n):
+    trees = all_trees(0, n)
+    rendered = [_render(t) for t in trees]
+    assert len(trees) == CATALAN[n - 1]
+    assert len(set(rendered)) == len(trees), "trees must be distinct"
+    for t in trees:
+        assert _leaves(t) == list(range(n)), "leaves in order, each once"
+    assert set(rendered) == _stack_parenthesisations(n)
+
+
+def test_all_trees_on_an_offset_range():
+    assert all_trees(3, 4) == [3]
+    assert all_trees(2, 4) == [(2, 3)]
+    assert sorted(map(_render, all_trees(4, 7))) == ["((4,5),6)", "(4,(5,6))"]
+
+
+@pytest.mark.parametrize("n", range(1, 7))
+def test_tree_reduce_follows_the_tree(n):
+    # A non-commutative, non-associative probe operation: the reduction
+    # must reproduce the tree's own bracketing, with left and right in place.
+    leaves = [str(i) for i in range(n)]
+    for t in all_trees(0, n):
+        got = tree_reduce(t, leaves, op=lambda a, b: "(" + a + "," + b + ")")
+        assert got == _render(t)
+
+
+def test_singleton_states():
+    assert singleton(2.5) == (2.5, 1.0)
+    assert singleton(-math.inf) == EMPTY_STATE
+    # One element through the recurrence: (x, e^(x - x)) = (x, 1).
+    assert online_state([-3.25]) == (-3.25, 1.0)
