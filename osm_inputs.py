@@ -112,6 +112,39 @@ def attention_grad_output(B, H, N, D, seed, device="cpu"):
     return torch.randn((B, H, N, D), generator=g, device=device).to(torch.bfloat16)
 
 
+def attention_rounding_inputs(B, H, N, D, seed, device="cpu"):
+    """Inputs that expose the rounding of the attention output.
+
+    Q = 0, so every visible key gets the same weight; K ~ N(0,1); V = 4 +
+    3.9 U(0,1) rounded to bfloat16, so V and every average of its rows lie in
+    [4, 8), where bfloat16 values are 2^-5 apart.  Drawn in the order K, V.
+    """
+    g = generator(seed, device)
+    shape = (B, H, N, D)
+    q = torch.zeros(shape, device=device, dtype=torch.bfloat16)
+    k = torch.randn(shape, generator=g, device=device).to(torch.bfloat16)
+    v = (4.0 + 3.9 * torch.rand(shape, generator=g, device=device)).to(torch.bfloat16)
+    return q, k, v
+
+
+#: Values of the constant V rows of ``attention_constant_v_inputs``: bfloat16
+#: numbers at the bottom (1, 2, 0.5) and top (255/128, 255/64) of a binade.
+CONSTANT_V_VALUES = (1.0, 255.0 / 128.0, 2.0, 255.0 / 64.0, 0.5, 255.0 / 256.0)
+
+
+def attention_constant_v_inputs(B, H, N, D, seed, device="cpu"):
+    """Q, K ~ N(0,1) (in that order) and V with every key row equal to one
+    vector c, whose entries cycle through ``CONSTANT_V_VALUES``."""
+    g = generator(seed, device)
+    shape = (B, H, N, D)
+    q = torch.randn(shape, generator=g, device=device).to(torch.bfloat16)
+    k = torch.randn(shape, generator=g, device=device).to(torch.bfloat16)
+    c = torch.tensor([CONSTANT_V_VALUES[d % len(CONSTANT_V_VALUES)] for d in range(D)],
+                     dtype=torch.bfloat16, device=device)
+    v = c.expand(shape).contiguous()
+    return q, k, v
+
+
 def attention_config(name, device="cpu", **override):
     """Inputs of one named attention workload; ``override`` changes sizes."""
     c = dict(ATTN_CONFIGS[name])

@@ -15,6 +15,7 @@ import torch
 import online_softmax_06_amd as osm
 import osm_inputs
 from oracle import attention_ref
+from tolerance import CONSTANT_V_MIN_KEYS, O_ABS_SLACK, bf16_rne_violations
 
 pytestmark = pytest.mark.gpu
 
@@ -187,3 +188,65 @@ def test_reference_moves_with_the_scores(slope, N, D, causal):
     o, lse = osm.attn_fwd(q, k, v, scale, causal)
     torch.cuda.synchronize()
     compare(q, k, v, scale, causal, o, lse)
+
+
+@pytest.mark.parametrize("D,N,causal", [(64, 300, False), (64, 300, True), (128, 1000, False),
+                                        (128, 1000, True), (128, 4100, True)])
+def test_output_rounds_to_nearest_even(D, N, causal):
+    # Q = 0: every visible key weighs exactly the same and O is the mean of
+    # the visible V rows, computed almost exactly in float32.  V in [4, 8)
+    # puts O where bfloat16 values are 2^-5 apart: rounding to nearest even
+    # stays within half of that, truncation errs by up to a whole step (and
+    # beyond the 2e-2 budget).  The 8-wavefront kernels run at D = 128 for
+    # unmasked rows and for causal rows of 4096 or more.
+    B, H = 1, 2
+    _announce("O rounding", B, H, N, D, causal)
+    q, k, v = osm_inputs.attention_rounding_inputs(B, H, N, D, seed=41, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = osm.attn_fwd(q, k, v, scale, causal)
+    torch.cuda.synchronize()
+    O, L = attention_ref(q.cpu().double().numpy(), k.cpu().double().numpy(),
+                         v.cpu().double().numpy(), scale, causal)
+    got = o.cpu().double().numpy()
+    bad = bf16_rne_violations(got, O, abs_slack=O_ABS_SLACK)
+    assert not bad.any(), f"{bad.sum()} outputs beyond the nearest-even bound"
+    assert np.abs(lse.cpu().double().numpy() - L).max() <= LSE_TOL
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_probabilities_round_to_nearest_even(D, causal):
+    # Every key row of V is the same vector c, so O = c whatever the weights.
+    # The kernel rounds P to bfloat16 before the P V product and divides by
+    # the sum of the unrounded P: with nearest-even rounding the errors of
+    # P average out over the keys and O rounds back to c exactly; truncated
+    # P would lose about 0.3% on every row and miss c (tests/test_tolerance.py
+    # shows both on the CPU for these inputs).
+    B, H, N = 1, 2, 1024
+    _announce("P rounding", B, H, N, D, causal)
+    q, k, v = osm_inputs.attention_constant_v_inputs(B, H, N, D, seed=43, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, _ = osm.attn_fwd(q, k, v, scale, causal)
+    torch.cuda.synchronize()
+    rows = slice(CONSTANT_V_MIN_KEYS - 1, None) if causal else slice(None)
+    got = o[:, :, rows]
+    want = v[:, :, :1].expand_as(got)
+    assert torch.equal(got, want), f"{(got != want).sum().item()} outputs differ from c"
+
+
+def test_raw_abi_attention_small_config():
+    # osm_attn_fwd itself (not the _ex form the tensor helper calls), raw
+    # through ctypes, on the small non-causal workload, compared in full.
+    cfg = osm_inputs.attention_config("attn_small", device="cuda")
+    c = cfg["cfg"]
+    _announce("raw osm_attn_fwd", c)
+    q, k, v = cfg["q"], cfg["k"], cfg["v"]
+    o = torch.empty_like(q)
+    lse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device="cuda")
+    st = osm.osm_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          lse.data_ptr(), c["B"], c["H"], c["N"], c["D"], cfg["scale"],
+                          int(cfg["causal"]), torch.cuda.current_stream().cuda_stream)
+    assert st == osm.OSM_OK, osm.osm_status_string(st)
+    torch.cuda.synchronize()
+    eo, el = compare(q, k, v, cfg["scale"], cfg["causal"], o, lse)
+    print(f"[result] raw osm_attn_fwd attn_small O err {eo:.3g} LSE err {el:.3g}", flush=True)

@@ -2,7 +2,8 @@
 
 osm_softmax_rows_split (a row shared by several workgroups, chunk states merged
 with the (m, l) combine) is held to the bars of the plain row softmax: float32
-1e-6 absolute, bfloat16 one bfloat16 ulp, hidden entries exactly 0.
+1e-6 absolute, bfloat16 half a bfloat16 ulp plus 2^-16 relative
+(tests/tolerance.py), hidden entries exactly 0.
 osm_attn_fwd_split (split-K with the log-sum-exp merge) is held to those of the
 fused attention: O 2e-2, LSE 1e-3, rows without a visible key give O = 0 and
 LSE = -inf.
@@ -16,6 +17,7 @@ import torch
 
 import online_softmax_06_amd as osm
 import osm_inputs
+from tolerance import bf16_rne_violations
 from oracle import attention_ref, masked_softmax_rows_ref
 
 pytestmark = pytest.mark.gpu
@@ -32,12 +34,6 @@ def _announce(*what):
     print("[case]", *what, flush=True)
 
 
-def _ulp(y):
-    y = np.abs(y)
-    e = np.floor(np.log2(np.where(y > 0, y, 1.0)))
-    return np.maximum(np.exp2(e - 7), 2.0 ** -133)
-
-
 def _check_softmax(x, mask, lens, y, dtype):
     ref = masked_softmax_rows_ref(x.double().numpy(),
                                   None if mask is None else mask.double().numpy(),
@@ -49,7 +45,7 @@ def _check_softmax(x, mask, lens, y, dtype):
     if dtype == torch.float32:
         assert err.max(initial=0) <= 1e-6, err.max()
     else:
-        assert (err <= _ulp(ref)).all(), err.max()
+        assert not bf16_rne_violations(got, ref).any(), err.max()
 
 
 # One chunk, a ragged second chunk, a scalar-path width, a 1M-element row.
