@@ -50,7 +50,7 @@ __all__ = [
     "osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split", "osm_attn_fwd_split_workspace",
     "osm_attn_bwd", "osm_attn_bwd_ex", "osm_attn_bwd_workspace",
     "osm_status_string", "osm_version", "softmax_rows",
-    "attn_fwd", "attn_bwd",
+    "attn_fwd", "attn_bwd", "check_tensor",
 ]
 
 OSM_F32, OSM_BF16 = 0, 1
@@ -216,6 +216,33 @@ def _dtype_code(dtype):
     raise TypeError(f"softmax_rows supports float32 and bfloat16, not {dtype}")
 
 
+def check_tensor(t, name, device, dtype, shape=None):
+    """Raise ValueError unless ``t`` is a contiguous tensor of ``dtype`` on
+    ``device`` (and of ``shape``, when given).
+
+    Every tensor a helper hands to the library goes through this check before
+    any launch: a kernel storing through a pointer that is not memory of the
+    launching device would fault the GPU.
+    """
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, not {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _gpu_device(t, name):
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t.device
+
+
 def softmax_rows(x, out=None, mask=None, row_len=None, split=False):
     """Softmax over the last dimension of a contiguous CUDA tensor.
 
@@ -228,28 +255,24 @@ def softmax_rows(x, out=None, mask=None, row_len=None, split=False):
     through torch's caching allocator).
     """
     torch = _torch()
-    if not x.is_cuda:
-        raise ValueError("softmax_rows needs a GPU tensor")
-    if not x.is_contiguous():
-        raise ValueError("softmax_rows needs a contiguous tensor")
+    dev = _gpu_device(x, "x")
     code = _dtype_code(x.dtype)
+    check_tensor(x, "x", dev, x.dtype)
     if out is None:
         out = torch.empty_like(x)
-    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() \
-            or out.device != x.device:
-        raise ValueError("out must be a contiguous tensor of the same shape, dtype and device")
+    check_tensor(out, "out", dev, x.dtype, x.shape)
     cols = x.shape[-1] if x.dim() > 0 else 1
     rows = x.numel() // cols if cols else 0
     mask_ptr, mask_rows, len_ptr = 0, 0, 0
     if mask is not None:
-        if not mask.is_cuda or mask.dtype != x.dtype or not mask.is_contiguous() \
-                or mask.shape[-1] != cols or mask.numel() == 0:
-            raise ValueError("mask must be a contiguous CUDA tensor of x's dtype ending in cols")
+        check_tensor(mask, "mask", dev, x.dtype)
+        if mask.dim() == 0 or mask.shape[-1] != cols or mask.numel() == 0:
+            raise ValueError("mask must end in the row length and hold at least one row")
         mask_ptr, mask_rows = mask.data_ptr(), mask.numel() // cols
     if row_len is not None:
-        if not row_len.is_cuda or row_len.dtype != torch.int32 or row_len.numel() != rows \
-                or not row_len.is_contiguous():
-            raise ValueError("row_len must be a contiguous int32 CUDA tensor with one entry per row")
+        check_tensor(row_len, "row_len", dev, torch.int32)
+        if row_len.numel() != rows:
+            raise ValueError(f"row_len must hold one entry per row ({rows})")
         len_ptr = row_len.data_ptr()
     if split:
         need = osm_softmax_rows_split_workspace(rows, cols)
@@ -280,31 +303,30 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None,
     torch's caching allocator).
     """
     torch = _torch()
+    dev = _gpu_device(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be a [B, H, N, D] tensor")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor [B, H, N, D]")
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k and v must have the same shape [B, H, N, D]")
+        check_tensor(t, name, dev, torch.bfloat16, q.shape)
     B, H, N, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    check_tensor(out, "out", dev, torch.bfloat16, q.shape)
+    check_tensor(lse, "lse", dev, torch.float32, (B, H, N))
     len_ptr, bias_ptr, sb, sh = 0, 0, 0, 0
     if kv_len is not None:
-        if not kv_len.is_cuda or kv_len.dtype != torch.int32 or kv_len.numel() != B \
-                or not kv_len.is_contiguous():
-            raise ValueError("kv_len must be a contiguous int32 CUDA tensor of length B")
+        check_tensor(kv_len, "kv_len", dev, torch.int32)
+        if kv_len.numel() != B:
+            raise ValueError(f"kv_len must hold one entry per batch ({B})")
         len_ptr = kv_len.data_ptr()
     if bias is not None:
-        if not bias.is_cuda or bias.dtype != torch.float32 or bias.dim() != 4:
-            raise ValueError("bias must be a float32 CUDA tensor [B or 1, H or 1, N, N]")
+        if not isinstance(bias, torch.Tensor) or bias.device != dev \
+                or bias.dtype != torch.float32 or bias.dim() != 4:
+            raise ValueError(f"bias must be a float32 tensor [B or 1, H or 1, N, N] on {dev}")
         bb = bias.expand(B, H, N, N)
         if bb.stride(3) != 1 or bb.stride(2) != N:
             raise ValueError("bias must have contiguous [N, N] trailing dims")
@@ -339,29 +361,26 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, 
     workspace is allocated here, through torch's caching allocator.
     """
     torch = _torch()
+    dev = _gpu_device(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be a [B, H, N, D] tensor")
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor [B, H, N, D]")
-        if t.shape != q.shape:
-            raise ValueError("q, k, v, o and dout must have the same shape [B, H, N, D]")
+        check_tensor(t, name, dev, torch.bfloat16, q.shape)
     B, H, N, D = q.shape
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
-            or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous float32 CUDA tensor [B, H, N]")
+    check_tensor(lse, "lse", dev, torch.float32, (B, H, N))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     grads = []
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is None:
             t = torch.empty_like(q)
-        elif t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous bfloat16 tensor shaped like q")
+        check_tensor(t, name, dev, torch.bfloat16, q.shape)
         grads.append(t)
     len_ptr = 0
     if kv_len is not None:
-        if not kv_len.is_cuda or kv_len.dtype != torch.int32 or kv_len.numel() != B \
-                or not kv_len.is_contiguous():
-            raise ValueError("kv_len must be a contiguous int32 CUDA tensor of length B")
+        check_tensor(kv_len, "kv_len", dev, torch.int32)
+        if kv_len.numel() != B:
+            raise ValueError(f"kv_len must hold one entry per batch ({B})")
         len_ptr = kv_len.data_ptr()
     need = osm_attn_bwd_workspace(B, H, N, D)
     if need < 0:

@@ -111,6 +111,71 @@ def test_tensor_helpers_reject_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         osm.attn_fwd(x, x, x)
+    with pytest.raises(ValueError):
+        osm.attn_bwd(x, x, x, x, torch.zeros(1, 1, 4), x)
+
+
+def test_check_tensor():
+    import torch
+    gpu = torch.device("cuda", 0)
+    cpu = torch.device("cpu")
+    t = torch.zeros(2, 3, dtype=torch.float32)
+    osm.check_tensor(t, "t", cpu, torch.float32, (2, 3))
+    with pytest.raises(ValueError, match="must be on cuda:0"):
+        osm.check_tensor(t, "t", gpu, torch.float32)
+    with pytest.raises(ValueError, match="dtype"):
+        osm.check_tensor(t, "t", cpu, torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        osm.check_tensor(t, "t", cpu, torch.float32, (3, 2))
+    with pytest.raises(ValueError, match="contiguous"):
+        osm.check_tensor(t.t(), "t", cpu, torch.float32)
+    with pytest.raises(ValueError, match="tensor"):
+        osm.check_tensor(None, "t", cpu, torch.float32)
+
+
+# Every tensor a helper passes on is checked against the first input's
+# device.  The helpers are run here with the inputs' device taken as given
+# (CPU) and one argument elsewhere ("meta"): each call must stop with
+# ValueError before the library is reached.
+def _on_meta(t):
+    import torch
+    return torch.empty(t.shape, dtype=t.dtype, device="meta")
+
+
+def test_helpers_check_every_tensor_device(monkeypatch):
+    import torch
+    monkeypatch.setattr(osm, "_gpu_device", lambda t, name: t.device)
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError, match="out must be on cpu"):
+        osm.softmax_rows(x, out=_on_meta(x))
+    with pytest.raises(ValueError, match="mask must be on cpu"):
+        osm.softmax_rows(x, mask=_on_meta(x))
+    with pytest.raises(ValueError, match="row_len must be on cpu"):
+        osm.softmax_rows(x, row_len=_on_meta(torch.zeros(4, dtype=torch.int32)))
+    q = torch.zeros(2, 1, 4, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(2, 1, 4)
+    kv = torch.zeros(2, dtype=torch.int32)
+    for kw in (dict(k=_on_meta(q)), dict(v=_on_meta(q))):
+        args = dict(q=q, k=q, v=q) | kw
+        with pytest.raises(ValueError, match="must be on cpu"):
+            osm.attn_fwd(args["q"], args["k"], args["v"])
+    for kw, name in ((dict(out=_on_meta(q)), "out"), (dict(lse=_on_meta(lse)), "lse"),
+                     (dict(kv_len=_on_meta(kv)), "kv_len"),
+                     (dict(bias=torch.zeros(1, 1, 4, 4, device="meta")), "bias")):
+        with pytest.raises(ValueError, match=f"{name} must"):
+            osm.attn_fwd(q, q, q, **kw)
+    for i, name in enumerate(("k", "v", "o", "dout")):
+        args = [q, q, q, q, lse, q]
+        args[[1, 2, 3, 5][i]] = _on_meta(q)
+        with pytest.raises(ValueError, match=f"{name} must be on cpu"):
+            osm.attn_bwd(*args)
+    with pytest.raises(ValueError, match="lse must be on cpu"):
+        osm.attn_bwd(q, q, q, q, _on_meta(lse), q)
+    for name in ("dq", "dk", "dv"):
+        with pytest.raises(ValueError, match=f"{name} must be on cpu"):
+            osm.attn_bwd(q, q, q, q, lse, q, **{name: _on_meta(q)})
+    with pytest.raises(ValueError, match="kv_len must be on cpu"):
+        osm.attn_bwd(q, q, q, q, lse, q, kv_len=_on_meta(kv))
 
 
 @pytest.mark.parametrize("args,expect", [
