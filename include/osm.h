@@ -279,6 +279,37 @@ int osm_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
  * rounded up to a multiple of 128); -1 for invalid arguments. */
 int64_t osm_attn_bwd_workspace(int B, int H, int N, int D);
 
+/*
+ * osm_attn_bwd_noalloc -- osm_attn_bwd_ex with no workspace argument, for
+ * callers that cannot allocate device memory: code being captured into a HIP
+ * graph, tight serving or training loops, and harnesses that forbid
+ * hipMalloc.  The call allocates and frees nothing.
+ *
+ * The per-row scratch (-Delta and LSE * log2 e, osm_attn_bwd_workspace bytes)
+ * lives in a fixed array of OSM_ATTN_BWD_SCRATCH_BYTES bytes inside the
+ * library.  Every GPU the library runs on holds its own copy from the first
+ * call on that GPU until the process ends.  Its content on entry does not
+ * matter: the first kernel writes every entry the second reads.  The call
+ * uses the array of the current device, which must be the device of the
+ * pointers and the stream.
+ *
+ * All calls on one GPU share that array: calls that overlap in time on one
+ * GPU (on different streams, or from host threads without ordering) race and
+ * give wrong gradients.  Calls ordered on one stream are safe.
+ *
+ *   q .. kv_len, stream   as osm_attn_bwd_ex.
+ *
+ * Returns as osm_attn_bwd_ex, plus OSM_ERR_UNSUPPORTED when
+ * osm_attn_bwd_workspace(B, H, N, D) exceeds OSM_ATTN_BWD_SCRATCH_BYTES
+ * (B * H * (N rounded up to 128) above 4194304 rows), checked before any HIP
+ * call, and OSM_ERR_HIP when the runtime cannot give the array's address.
+ */
+#define OSM_ATTN_BWD_SCRATCH_BYTES ((int64_t)32 << 20)
+int osm_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                         int H, int N, int D, float scale, int causal, const int32_t* kv_len,
+                         void* stream);
+
 /* Human-readable name of a status code; never NULL, static storage. */
 const char* osm_status_string(int status);
 

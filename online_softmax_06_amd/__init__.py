@@ -25,6 +25,8 @@ ints; ``stream`` is a hipStream_t handle, 0 for the null stream):
     osm_attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
                     causal, kv_len, workspace, workspace_bytes, stream) -> status
     osm_attn_bwd_workspace(B, H, N, D) -> bytes
+    osm_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
+                         causal, kv_len, stream) -> status
     osm_status_string(status) -> str
 
 Tensor-level helpers:
@@ -48,13 +50,15 @@ __all__ = [
     "OsmError", "lib_path", "load_library", "osm_softmax_rows", "osm_softmax_rows_ex",
     "osm_softmax_rows_split", "osm_softmax_rows_split_workspace",
     "osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split", "osm_attn_fwd_split_workspace",
-    "osm_attn_bwd", "osm_attn_bwd_ex", "osm_attn_bwd_workspace",
+    "osm_attn_bwd", "osm_attn_bwd_ex", "osm_attn_bwd_workspace", "osm_attn_bwd_noalloc",
+    "OSM_ATTN_BWD_SCRATCH_BYTES",
     "osm_status_string", "osm_version", "softmax_rows",
     "attn_fwd", "attn_bwd", "check_tensor",
 ]
 
 OSM_F32, OSM_BF16 = 0, 1
 OSM_OK, OSM_ERR_INVALID_ARG, OSM_ERR_UNSUPPORTED, OSM_ERR_HIP = 0, 1, 2, 3
+OSM_ATTN_BWD_SCRATCH_BYTES = 32 << 20  # include/osm.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -111,6 +115,9 @@ def load_library():
     lib.osm_attn_bwd_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int,
                                     c_int, c_int, c_int, c_f, c_int, c_vp, c_vp, c_i64, c_vp]
     lib.osm_attn_bwd_ex.restype = c_int
+    lib.osm_attn_bwd_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                         c_int, c_int, c_int, c_int, c_f, c_int, c_vp, c_vp]
+    lib.osm_attn_bwd_noalloc.restype = c_int
     lib.osm_attn_bwd_workspace.argtypes = [c_int, c_int, c_int, c_int]
     lib.osm_attn_bwd_workspace.restype = c_i64
     lib.osm_status_string.argtypes = [c_int]
@@ -179,6 +186,12 @@ def osm_attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale, causal
                     workspace, workspace_bytes, stream=0):
     return load_library().osm_attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
                                           int(causal), kv_len, workspace, workspace_bytes, stream)
+
+
+def osm_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale, causal,
+                         kv_len=0, stream=0):
+    return load_library().osm_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D,
+                                               scale, int(causal), kv_len or None, stream)
 
 
 def osm_attn_bwd_workspace(B, H, N, D):

@@ -43,10 +43,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "osm_device.h"
 #include "osm_internal.h"
+
+// Scratch memory of the allocation-free backward (osm_attn_bwd_noalloc): the
+// per-row -Delta and LSE * log2 e arrays live here instead of in a caller's
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host it names a stand-in, not device memory): it uses the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[osm::kAttnBwdScratchBytes];
 
 namespace osm {
 namespace {
@@ -675,6 +684,28 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
 int64_t attn_bwd_workspace(int B, int H, int N) {
   const int64_t Np = ((int64_t)N + kPad - 1) / kPad * kPad;
   return 2 * 4 * (int64_t)B * H * Np;
+}
+
+hipError_t attn_bwd_scratch(void** ptr) {
+  // One lookup per device, with that device current; the addresses are
+  // kept for the life of the process.
+  constexpr int kMaxDevices = 64;
+  static std::mutex lock;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> guard(lock);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t attn_bwd_launch(const void* q, const void* k, const void* v, const void* o,

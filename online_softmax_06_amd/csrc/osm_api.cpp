@@ -8,6 +8,9 @@
 #include "osm.h"
 #include "osm_internal.h"
 
+static_assert(OSM_ATTN_BWD_SCRATCH_BYTES == osm::kAttnBwdScratchBytes,
+              "the header states the size of the library's scratch array");
+
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -184,6 +187,25 @@ int osm_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
     return OSM_ERR_INVALID_ARG;
   return from_hip(osm::attn_bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
                                        causal != 0, kv_len, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int osm_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                         int H, int N, int D, float scale, int causal, const int32_t* kv_len,
+                         void* stream) {
+  const int st = check_attn(q, k, v, o, lse, B, H, N, D, scale, kv_len, nullptr, 0, 0, 1);
+  if (st != OSM_OK || (int64_t)B * H * N == 0) return st;
+  if (!dout || !dq || !dk || !dv) return OSM_ERR_INVALID_ARG;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return OSM_ERR_INVALID_ARG;
+  const int64_t need = osm_attn_bwd_workspace(B, H, N, D);
+  if (need < 0) return OSM_ERR_INVALID_ARG;
+  if (need > OSM_ATTN_BWD_SCRATCH_BYTES) return OSM_ERR_UNSUPPORTED;
+  void* scratch = nullptr;
+  if (osm::attn_bwd_scratch(&scratch) != hipSuccess) return OSM_ERR_HIP;
+  return from_hip(osm::attn_bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
+                                       causal != 0, kv_len, scratch,
                                        static_cast<hipStream_t>(stream)));
 }
 

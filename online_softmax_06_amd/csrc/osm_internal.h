@@ -46,6 +46,12 @@ hipError_t attn_fwd_split_launch(const void* q, const void* k, const void* v, vo
 // two kernels (dQ, which also fills the workspace, then dK/dV).  D must be 64 or 128; kv_len (nullable,
 // int32 [B]) limits the keys of each batch as in the forward.
 int64_t attn_bwd_workspace(int B, int H, int N);
+
+// Size of the library's own scratch array for the allocation-free backward
+// (one per GPU), and its device address on the current device (looked up
+// once per device; hipSuccess or the runtime's error).
+constexpr int64_t kAttnBwdScratchBytes = (int64_t)32 << 20;
+hipError_t attn_bwd_scratch(void** ptr);
 hipError_t attn_bwd_launch(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
                            int H, int N, int D, float scale, bool causal, const int32_t* kv_len,

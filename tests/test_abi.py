@@ -31,7 +31,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["osm_attn_bwd", "osm_attn_bwd_ex", "osm_attn_bwd_workspace",
+    assert _declared_functions() == ["osm_attn_bwd", "osm_attn_bwd_ex", "osm_attn_bwd_noalloc",
+                                     "osm_attn_bwd_workspace",
                                      "osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split",
                                      "osm_attn_fwd_split_workspace", "osm_softmax_rows",
                                      "osm_softmax_rows_ex", "osm_softmax_rows_split",
@@ -276,3 +277,23 @@ def test_attn_bwd_ex_checks_kv_len_alignment(lib):
         osm.OSM_ERR_INVALID_ARG
     assert osm.osm_attn_bwd_ex(*p, 1, 2, 300, 96, 0.1, 1, 0, FAKE, 1 << 30, 0) == \
         osm.OSM_ERR_UNSUPPORTED
+
+
+def _bwd_noalloc(B=1, H=1, N=64, D=64):
+    return osm.osm_attn_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    B, H, N, D, 0.125, 1, 0, 0)
+
+
+def test_noalloc_backward_size_limit(lib):
+    # The scratch array holds 8 bytes per padded query row: B * H * (N rounded
+    # up to 128) <= 4194304.  Larger calls are refused before any HIP call.
+    assert osm.OSM_ATTN_BWD_SCRATCH_BYTES == 32 << 20
+    assert osm.osm_attn_bwd_workspace(1, 32768, 128, 64) == osm.OSM_ATTN_BWD_SCRATCH_BYTES
+    assert _bwd_noalloc(B=1, H=32769, N=128) == osm.OSM_ERR_UNSUPPORTED
+    assert _bwd_noalloc(B=8, H=40, N=16384, D=128) == osm.OSM_ERR_UNSUPPORTED
+    assert _bwd_noalloc(B=2, H=16385, N=100) == osm.OSM_ERR_UNSUPPORTED  # 100 pads to 128
+    assert _bwd_noalloc(D=96) == osm.OSM_ERR_UNSUPPORTED
+    assert _bwd_noalloc(B=-1) == osm.OSM_ERR_INVALID_ARG
+    assert osm.osm_attn_bwd_noalloc(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    1, 1, 64, 64, 0.125, 1, 0, 0) == osm.OSM_ERR_INVALID_ARG
+    assert _bwd_noalloc(N=0) == osm.OSM_OK
