@@ -310,6 +310,23 @@ int osm_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void
                          int H, int N, int D, float scale, int causal, const int32_t* kv_len,
                          void* stream);
 
+/*
+ * osm_stream_copy -- copy `bytes` bytes from src to dst on the device with
+ * the memory access pattern of the row softmax (16-byte non-temporal loads
+ * and stores, every byte read once and written once).  A measurement
+ * utility, not a step of the method: its rate on the softmax's bytes is the
+ * practical ceiling of a kernel that moves one read and one write per
+ * element, the traffic [Ch6 §6.2] and [Ch6 §6.7.4] give as the softmax's
+ * lower bound.
+ *
+ *   src, dst  device pointers, 16-byte aligned; the ranges must not overlap.
+ *   bytes     0 .. 2^44 (0 is a no-op).
+ *
+ * Returns OSM_OK, OSM_ERR_INVALID_ARG (null or misaligned pointer,
+ * overlapping ranges, size out of range) or OSM_ERR_HIP.
+ */
+int osm_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 /* Human-readable name of a status code; never NULL, static storage. */
 const char* osm_status_string(int status);
 

@@ -27,6 +27,7 @@ ints; ``stream`` is a hipStream_t handle, 0 for the null stream):
     osm_attn_bwd_workspace(B, H, N, D) -> bytes
     osm_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale,
                          causal, kv_len, stream) -> status
+    osm_stream_copy(src, dst, bytes, stream) -> status   (bandwidth ceiling probe)
     osm_status_string(status) -> str
 
 Tensor-level helpers:
@@ -51,7 +52,7 @@ __all__ = [
     "osm_softmax_rows_split", "osm_softmax_rows_split_workspace",
     "osm_attn_fwd", "osm_attn_fwd_ex", "osm_attn_fwd_split", "osm_attn_fwd_split_workspace",
     "osm_attn_bwd", "osm_attn_bwd_ex", "osm_attn_bwd_workspace", "osm_attn_bwd_noalloc",
-    "OSM_ATTN_BWD_SCRATCH_BYTES",
+    "OSM_ATTN_BWD_SCRATCH_BYTES", "osm_stream_copy",
     "osm_status_string", "osm_version", "softmax_rows",
     "attn_fwd", "attn_bwd", "check_tensor",
 ]
@@ -120,6 +121,8 @@ def load_library():
     lib.osm_attn_bwd_noalloc.restype = c_int
     lib.osm_attn_bwd_workspace.argtypes = [c_int, c_int, c_int, c_int]
     lib.osm_attn_bwd_workspace.restype = c_i64
+    lib.osm_stream_copy.argtypes = [c_vp, c_vp, c_i64, c_vp]
+    lib.osm_stream_copy.restype = c_int
     lib.osm_status_string.argtypes = [c_int]
     lib.osm_status_string.restype = ctypes.c_char_p
     lib.osm_version.argtypes = []
@@ -196,6 +199,10 @@ def osm_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, scale, c
 
 def osm_attn_bwd_workspace(B, H, N, D):
     return load_library().osm_attn_bwd_workspace(B, H, N, D)
+
+
+def osm_stream_copy(src, dst, nbytes, stream=0):
+    return load_library().osm_stream_copy(src, dst, nbytes, stream)
 
 
 def osm_status_string(status):

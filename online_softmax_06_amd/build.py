@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libosm.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["osm_api.cpp", "softmax_rows.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["osm_api.cpp", "softmax_rows.hip", "attn_fwd.hip", "attn_bwd.hip", "stream_copy.hip"]
 
 ARCH = "gfx950"
 

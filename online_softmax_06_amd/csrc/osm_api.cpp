@@ -85,6 +85,16 @@ int osm_softmax_rows_split(const void* in, void* out, int64_t rows, int64_t cols
                                                  static_cast<hipStream_t>(stream)));
 }
 
+int osm_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes > ((int64_t)1 << 44)) return OSM_ERR_INVALID_ARG;
+  if (bytes == 0) return OSM_OK;
+  if (src == nullptr || dst == nullptr) return OSM_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return OSM_ERR_INVALID_ARG;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + (uint64_t)bytes && b < a + (uint64_t)bytes) return OSM_ERR_INVALID_ARG;
+  return from_hip(osm::stream_copy_launch(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
 int osm_softmax_rows(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
                      void* stream) {
   return osm_softmax_rows_ex(in, out, rows, cols, dtype, nullptr, 0, nullptr, stream);

@@ -57,4 +57,8 @@ hipError_t attn_bwd_launch(const void* q, const void* k, const void* v, const vo
                            int H, int N, int D, float scale, bool causal, const int32_t* kv_len,
                            void* workspace, hipStream_t stream);
 
+// Streaming copy of `bytes` bytes (16-byte aligned src and dst), the
+// practical bandwidth ceiling of one read and one write per byte.
+hipError_t stream_copy_launch(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 }  // namespace osm

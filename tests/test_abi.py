@@ -37,6 +37,7 @@ def test_header_declares_the_boundary():
                                      "osm_attn_fwd_split_workspace", "osm_softmax_rows",
                                      "osm_softmax_rows_ex", "osm_softmax_rows_split",
                                      "osm_softmax_rows_split_workspace", "osm_status_string",
+                                     "osm_stream_copy",
                                      "osm_version"]
 
 
@@ -297,3 +298,16 @@ def test_noalloc_backward_size_limit(lib):
     assert osm.osm_attn_bwd_noalloc(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                     1, 1, 64, 64, 0.125, 1, 0, 0) == osm.OSM_ERR_INVALID_ARG
     assert _bwd_noalloc(N=0) == osm.OSM_OK
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((FAKE, FAKE + (1 << 20), -1), osm.OSM_ERR_INVALID_ARG),      # negative size
+    ((FAKE, FAKE + (1 << 20), (1 << 44) + 1), osm.OSM_ERR_INVALID_ARG),  # too large
+    ((0, FAKE, 64), osm.OSM_ERR_INVALID_ARG),                      # null source
+    ((FAKE + 8, FAKE + (1 << 20), 64), osm.OSM_ERR_INVALID_ARG),   # misaligned
+    ((FAKE, FAKE + 32, 64), osm.OSM_ERR_INVALID_ARG),              # overlapping
+    ((FAKE + 32, FAKE, 64), osm.OSM_ERR_INVALID_ARG),              # overlapping
+    ((0, 0, 0), osm.OSM_OK),                                       # empty: no-op
+])
+def test_stream_copy_argument_checks(lib, args, expect):
+    assert osm.osm_stream_copy(*args, 0) == expect
