@@ -6,26 +6,36 @@ One step is one pass of the whole path over resident synthetic inputs:
   3. fused causal attention forward, bfloat16, B=8 H=40 N=2048 D=128
      (LLaMA-2-13B-shaped layer; bound by the bf16 matrix cores)
 
-Also timed, outside the step (its own loop over the same number of launches):
+Also timed, outside the step (each in its own loop of the same number of
+launches, reported in ``rooflines`` with ``"in_step": false``):
   4. attention backward (dQ, dK, dV from the forward's O and LSE) on the same
-     layer, reported under ``attention_backward`` and in ``rooflines`` with
-     ``"in_step": false``.
+     layer, also under ``attention_backward``;
+  5. the long-context causal forward, B=1 H=32 N=16384 D=128;
+  6. the small non-causal forward, B=1 H=8 N=1024 D=64 (64 query tiles for
+     256 compute units and a cache-resident working set: latency-bound);
+  7. the small softmax workload, its three calls (62 x 1000, 2 x 100, 1 x 3),
+     a latency figure per call;
+  8. ``osm_stream_copy`` of the float32 softmax bytes (1 GiB read + 1 GiB
+     written), the practical streaming ceiling, interleaved launch by launch
+     with the float32 softmax so that both see the same clock.
 
 Printed: one JSON line.  ``value`` is the softmax throughput of the
 bandwidth-scale workload (algorithmic bytes of both softmax runs / their
 kernel time); the attention throughput is in ``attention``.  ``rooflines``
 holds each kernel against its roofline; ``roofline`` repeats the kernel that
 takes the largest share of a step.  Kernel times come from HIP events recorded
-on the launch stream around every launch of the timed steps.
+on the launch stream around every launch.
 
-Context fields: ``copy_ceiling`` is the fastest of 20 device-to-device
-``hipMemcpyAsync`` calls on the float32 softmax bytes, with their median (the
-practical streaming ceiling the softmax runs are compared with) and ``sclk_mhz`` the engine clock read from the driver's
-``pp_dpm_sclk`` while the timed steps run (null where the file is absent).
+``parity`` holds the largest error of the timed outputs against the float64
+oracle for each workload (on the sample the ``cpu_baseline`` leg runs), and
+``cpu_baseline`` the oracle's own rate on that sample, with full-size
+estimates for the large attention workloads.  ``copy_ceiling`` summarises
+unit 8 next to the float32 softmax; ``sclk_mhz`` is the engine clock read from
+the driver's ``pp_dpm_sclk`` while the timed steps run.
 
-``--only`` runs a single unit (for profiler runs; ``attn_long``, the B1 H32
-N16384 D128 causal workload, runs only this way); ``--copy`` times a plain
-device copy of the float32 softmax bytes (the counter calibration kernel).
+``--only`` runs a single unit (for profiler runs); ``--copy`` times a plain
+runtime device copy of the float32 softmax bytes (the counter calibration
+kernel).
 """
 
 import argparse
@@ -48,6 +58,9 @@ BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16: 256 CU x 4096 FLOP/clk x 2.
 METRIC = "softmax GB/s (% HBM peak); attention fwd TFLOPS (% bf16 MFMA peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 SRC_DIR = os.path.join(ROOT, "online_softmax_06_amd", "csrc")
+
+UNIT_NAMES = ["softmax_f32", "softmax_bf16", "attn", "attn_bwd", "attn_long", "attn_small",
+              "softmax_small", "copy_f32"]
 
 
 def kernel_source_hash(fname):
@@ -76,58 +89,59 @@ def read_traffic():
 
 
 class Unit:
-    def __init__(self, name, kernel, src, launch, work, bound, peak, unit, workload, in_step=True):
+    def __init__(self, name, kernel, src, launch, work, bound, peak, unit, workload,
+                 in_step=True, note=None, pair=None):
         self.name, self.kernel, self.src = name, kernel, src
         self.launch, self.work, self.bound, self.peak = launch, work, bound, peak
-        self.unit, self.workload, self.in_step = unit, workload, in_step
+        self.unit, self.workload, self.in_step, self.note = unit, workload, in_step, note
+        self.pair = pair  # name of a unit to interleave with, launch by launch
         self.times_ms = []
+        self.data = {}    # inputs and outputs kept for the parity check
+
+
+def causal_pairs(N, causal):
+    return N * (N + 1) // 2 if causal else N * N
+
+
+def attn_unit(torch, osm, osm_inputs, name, kernel, in_step, note=None):
+    cfg = osm_inputs.attention_config(name, device="cuda")
+    a = cfg["cfg"]
+    o = torch.empty_like(cfg["q"])
+    lse = torch.empty((a["B"], a["H"], a["N"]), dtype=torch.float32, device="cuda")
+    # Algorithmic FLOPs: QK^T and PV over the unmasked (query, key) pairs,
+    # 2 * 2 * D per pair.
+    flops = 4 * a["D"] * causal_pairs(a["N"], a["causal"]) * a["B"] * a["H"]
+    u = Unit(name, kernel, "attn_fwd.hip",
+             (lambda cfg=cfg, o=o, lse=lse: osm.attn_fwd(cfg["q"], cfg["k"], cfg["v"], cfg["scale"],
+                                                         cfg["causal"], out=o, lse=lse)),
+             flops, "mfma", BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
+             f"{name} B{a['B']} H{a['H']} N{a['N']} D{a['D']} "
+             f"{'causal' if a['causal'] else 'non-causal'}", in_step=in_step, note=note)
+    u.data = dict(cfg=cfg, o=o, lse=lse)
+    return u
 
 
 def make_units(torch, osm, osm_inputs, only):
     units = []
+    want = lambda n: only in (None, n)  # noqa: E731
     c = osm_inputs.SOFTMAX_LARGE
     for dt, tag in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
         name = f"softmax_{tag}"
-        if only not in (None, name):
+        if not want(name):
             continue
         x = osm_inputs.softmax_large(dtype=dt, device="cuda")
         y = torch.empty_like(x)
         nbytes = 2 * x.numel() * x.element_size()  # one read + one write per element
-        units.append(Unit(
-            name, f"softmax_resident_kernel ({tag})", "softmax_rows.hip",
-            (lambda x=x, y=y: osm.softmax_rows(x, out=y)), nbytes, "hbm", HBM_PEAK_GBS, "GB/s",
-            f"softmax_large {c['rows']}x{c['cols']} {tag}"))
-    if only in (None, "attn"):
-        cfg = osm_inputs.attention_config("attn_llama13b", device="cuda")
-        a = cfg["cfg"]
-        o = torch.empty_like(cfg["q"])
-        lse = torch.empty((a["B"], a["H"], a["N"]), dtype=torch.float32, device="cuda")
-        # Algorithmic FLOPs: QK^T and PV over the unmasked (query, key) pairs,
-        # 2 * 2 * D per pair; causal pairs = N (N + 1) / 2 per head.
-        pairs = a["N"] * (a["N"] + 1) // 2 if a["causal"] else a["N"] * a["N"]
-        flops = 4 * a["D"] * pairs * a["B"] * a["H"]
-        units.append(Unit(
-            "attn", "attn_fwd_kernel<128, causal>", "attn_fwd.hip",
-            (lambda cfg=cfg, o=o, lse=lse: osm.attn_fwd(cfg["q"], cfg["k"], cfg["v"], cfg["scale"],
-                                                        cfg["causal"], out=o, lse=lse)),
-            flops, "mfma", BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
-            f"attn_llama13b B{a['B']} H{a['H']} N{a['N']} D{a['D']} causal"))
-    if only == "attn_long":
-        # Profiling only (never part of the default step): the long-context
-        # causal workload, B1 H32 N16384 D128, for its counters.
-        cfg = osm_inputs.attention_config("attn_long", device="cuda")
-        a = cfg["cfg"]
-        o = torch.empty_like(cfg["q"])
-        lse = torch.empty((a["B"], a["H"], a["N"]), dtype=torch.float32, device="cuda")
-        pairs = a["N"] * (a["N"] + 1) // 2 if a["causal"] else a["N"] * a["N"]
-        flops = 4 * a["D"] * pairs * a["B"] * a["H"]
-        units.append(Unit(
-            "attn_long", "attn_fwd_kernel<128, causal> (8 wavefronts)", "attn_fwd.hip",
-            (lambda cfg=cfg, o=o, lse=lse: osm.attn_fwd(cfg["q"], cfg["k"], cfg["v"], cfg["scale"],
-                                                        cfg["causal"], out=o, lse=lse)),
-            flops, "mfma", BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
-            f"attn_long B{a['B']} H{a['H']} N{a['N']} D{a['D']} causal", in_step=False))
-    if only in (None, "attn_bwd"):
+        u = Unit(name, f"softmax_resident_kernel ({tag})", "softmax_rows.hip",
+                 (lambda x=x, y=y: osm.softmax_rows(x, out=y)), nbytes, "hbm", HBM_PEAK_GBS,
+                 "GB/s", f"softmax_large {c['rows']}x{c['cols']} {tag}")
+        u.data = dict(x=x, y=y)
+        units.append(u)
+    if want("attn"):
+        units.append(attn_unit(torch, osm, osm_inputs, "attn_llama13b",
+                               "attn_fwd_kernel<128, causal>", True))
+        units[-1].name = "attn"
+    if want("attn_bwd"):
         cfg = osm_inputs.attention_config("attn_llama13b", device="cuda")
         a = cfg["cfg"]
         do = osm_inputs.attention_grad_output(a["B"], a["H"], a["N"], a["D"], seed=a["seed"],
@@ -136,82 +150,237 @@ def make_units(torch, osm, osm_inputs, only):
         grads = [torch.empty_like(cfg["q"]) for _ in range(3)]
         # Algorithmic FLOPs: the five products of the backward (S recomputed,
         # dP, dV, dK, dQ), 2 * D each per unmasked (query, key) pair.
-        pairs = a["N"] * (a["N"] + 1) // 2 if a["causal"] else a["N"] * a["N"]
-        flops = 10 * a["D"] * pairs * a["B"] * a["H"]
+        flops = 10 * a["D"] * causal_pairs(a["N"], a["causal"]) * a["B"] * a["H"]
+        u = Unit("attn_bwd", "attn_bwd dq + dkdv kernels <128, causal>", "attn_bwd.hip",
+                 (lambda cfg=cfg, o=o, lse=lse, do=do, g=grads: osm.attn_bwd(
+                     cfg["q"], cfg["k"], cfg["v"], o, lse, do, scale=cfg["scale"],
+                     causal=cfg["causal"], dq=g[0], dk=g[1], dv=g[2])),
+                 flops, "mfma", BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
+                 f"attn_llama13b B{a['B']} H{a['H']} N{a['N']} D{a['D']} causal, backward",
+                 in_step=False)
+        u.data = dict(cfg=cfg, do=do, grads=grads)
+        units.append(u)
+    if want("attn_long"):
+        units.append(attn_unit(torch, osm, osm_inputs, "attn_long",
+                               "attn_fwd_kernel<128, causal> (8 wavefronts)", False))
+    if want("attn_small"):
+        units.append(attn_unit(
+            torch, osm, osm_inputs, "attn_small", "attn_fwd_kernel<64, non-causal>", False,
+            note="latency-bound: 64 query tiles for 256 compute units, cache-resident inputs"))
+    if want("softmax_small"):
+        d = osm_inputs.softmax_small()
+        calls = [(label, x.cuda(), torch.empty_like(x, device="cuda")) for label, x in d["calls"]]
+        nbytes = sum(2 * x.numel() * 4 for _, x, _ in calls)
+
+        def run_small(calls=calls):
+            for _, x, y in calls:
+                osm.softmax_rows(x, out=y)
+        u = Unit("softmax_small", "softmax_resident_kernel (f32), three calls", "softmax_rows.hip",
+                 run_small, nbytes, "hbm", HBM_PEAK_GBS, "GB/s",
+                 "softmax_small 62x1000 + 2x100 + 1x3 f32", in_step=False,
+                 note="latency-bound: three launches of 62, 2 and 1 rows; avg_ms covers all three")
+        u.data = dict(calls=calls)
+        units.append(u)
+    if only in (None, "copy_f32"):
+        x = osm_inputs.softmax_large(device="cuda")
+        y = torch.empty_like(x)
+        nbytes = x.numel() * 4
+        stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+
+        def run_copy(x=x, y=y):
+            st = osm.osm_stream_copy(x.data_ptr(), y.data_ptr(), nbytes, stream())
+            if st != osm.OSM_OK:
+                raise osm.OsmError(st, "osm_stream_copy")
         units.append(Unit(
-            "attn_bwd", "attn_bwd dq + dkdv kernels <128, causal>", "attn_bwd.hip",
-            (lambda cfg=cfg, o=o, lse=lse, do=do, g=grads: osm.attn_bwd(
-                cfg["q"], cfg["k"], cfg["v"], o, lse, do, scale=cfg["scale"],
-                causal=cfg["causal"], dq=g[0], dk=g[1], dv=g[2])),
-            flops, "mfma", BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
-            f"attn_llama13b B{a['B']} H{a['H']} N{a['N']} D{a['D']} causal, backward",
-            in_step=False))
+            "copy_f32", "stream_copy_kernel", "stream_copy.hip", run_copy, 2 * nbytes, "hbm",
+            HBM_PEAK_GBS, "GB/s", f"copy of softmax_large {c['rows']}x{c['cols']} f32 bytes",
+            in_step=False, pair="softmax_f32" if only is None else None))
     return units
 
 
-def cpu_baseline(torch, osm_inputs, budget_s):
-    """Time the float64 oracle on bounded samples of the same workloads."""
+# ---------------------------------------------------------------------------
+# Oracle leg: rate of the float64 oracle on bounded samples, and the largest
+# error of the timed outputs on the same samples.
+# ---------------------------------------------------------------------------
+
+def _rne_bound(ref):
     import numpy as np
-    from oracle import attention_ref, softmax_rows_ref
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return 0.5 * np.maximum(np.exp2(e - 7), 2.0 ** -133) + 2.0 ** -15 * a
+
+
+def oracle_leg(torch, osm_inputs, units, budget_s):
+    import numpy as np
+    from oracle import (attention_bwd_head_ref, attention_head_ref, attention_ref,
+                        softmax_rows_ref)
     try:
         import threadpoolctl
         blas_threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info())
     except Exception:
         blas_threads = None
+    by = {u.name: u for u in units}
+    parity, cpu = {}, {}
+
+    # cfg1: the three small calls in full.
+    if "softmax_small" in by:
+        err = 0.0
+        for label, x, y in by["softmax_small"].data["calls"]:
+            ref = softmax_rows_ref(x.double().cpu().numpy())
+            err = max(err, float(np.abs(y.double().cpu().numpy() - ref).max()))
+        parity["softmax_small"] = {"max_abs_err": err, "tol": 1e-6, "sample": "all three calls"}
+
+    # cfg2, float32: the oracle timed on whole 1024-row chunks, and compared.
     c = osm_inputs.SOFTMAX_LARGE
-    x = osm_inputs.softmax_large(device="cuda")
-    rows_done, t_sm = 0, 0.0
-    chunk = 1024
-    while rows_done < c["rows"] and t_sm < budget_s * 0.5:
-        xs = x[rows_done:rows_done + chunk].double().cpu().numpy()
-        t0 = time.perf_counter()
-        softmax_rows_ref(xs)
-        t_sm += time.perf_counter() - t0
-        rows_done += xs.shape[0]
-    del x
-    sm_bytes = 2 * rows_done * c["cols"] * 4
-    cfg = osm_inputs.attention_config("attn_llama13b", device="cuda")
-    a = cfg["cfg"]
-    heads = osm_inputs.sample_heads(a["B"], a["H"], a["B"] * a["H"], a["seed"], [(0, 0)])
-    done, t_at = [], 0.0
-    for (b, h) in heads:
-        if t_at >= budget_s * 0.25:
-            break
-        q, k, v = (cfg[n][b, h][None, None].double().cpu().numpy() for n in ("q", "k", "v"))
-        t0 = time.perf_counter()
-        attention_ref(q, k, v, cfg["scale"], True)
-        t_at += time.perf_counter() - t0
-        done.append((b, h))
-    at_flops = 4 * a["D"] * (a["N"] * (a["N"] + 1) // 2) * len(done)
-    from oracle import attention_bwd_head_ref
-    do = osm_inputs.attention_grad_output(a["B"], a["H"], a["N"], a["D"], seed=a["seed"],
-                                          device="cuda")
-    done_b, t_bw = [], 0.0
-    for (b, h) in heads:
-        if t_bw >= budget_s * 0.25:
-            break
-        q, k, v, g = (t[b, h].double().cpu().numpy() for t in (cfg["q"], cfg["k"], cfg["v"], do))
-        t0 = time.perf_counter()
-        attention_bwd_head_ref(q, k, v, g, cfg["scale"], True)
-        t_bw += time.perf_counter() - t0
-        done_b.append((b, h))
-    bw_flops = 10 * a["D"] * (a["N"] * (a["N"] + 1) // 2) * len(done_b)
-    return {
-        "value": round(sm_bytes / t_sm / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"float64 three-pass softmax oracle (numpy, single-threaded) on the first "
-                   f"{rows_done} of {c['rows']} rows of softmax_large fp32 ({t_sm:.1f} s)"),
-        "attention": {
-            "value": round(at_flops / t_at / 1e12, 6), "unit": "TFLOP/s",
+    if "softmax_f32" in by:
+        x, y = by["softmax_f32"].data["x"], by["softmax_f32"].data["y"]
+        rows_done, t_sm, err, rel = 0, 0.0, 0.0, 0.0
+        while rows_done < c["rows"] and t_sm < budget_s * 0.3:
+            xs = x[rows_done:rows_done + 1024].double().cpu().numpy()
+            t0 = time.perf_counter()
+            ref = softmax_rows_ref(xs)
+            t_sm += time.perf_counter() - t0
+            d = np.abs(y[rows_done:rows_done + 1024].double().cpu().numpy() - ref)
+            err = max(err, float(d.max()))
+            nz = ref > 0
+            rel = max(rel, float((d[nz] / ref[nz]).max()))
+            rows_done += xs.shape[0]
+        cpu.update({
+            "value": round(2 * rows_done * c["cols"] * 4 / t_sm / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": (f"float64 three-pass softmax oracle (numpy, single-threaded) on the first "
+                       f"{rows_done} of {c['rows']} rows of softmax_large fp32 ({t_sm:.1f} s)")})
+        parity["softmax_large_f32"] = {"max_abs_err": err, "tol": 1e-6, "max_rel_err": rel,
+                                       "sample": f"first {rows_done} of {c['rows']} rows"}
+    if "softmax_bf16" in by:
+        x, y = by["softmax_bf16"].data["x"], by["softmax_bf16"].data["y"]
+        g = torch.Generator().manual_seed(2024)
+        rows = torch.cat([torch.tensor([0, c["rows"] - 1]),
+                          torch.randint(1, c["rows"] - 1, (1022,), generator=g)]).cuda()
+        ref = softmax_rows_ref(x[rows].double().cpu().numpy())
+        got = y[rows].double().cpu().numpy()
+        e = np.abs(got - ref)
+        parity["softmax_large_bf16"] = {
+            "max_abs_err": float(e.max()),
+            "max_err_over_rne_bound": float((e / _rne_bound(ref)).max()),
+            "tol": "half a bf16 ulp + 2^-15 relative (ratio <= 1)",
+            "sample": "1024 seeded rows incl. the first and last"}
+
+    def attn_err(u, heads, rows=None):
+        cfg, o, lse = u.data["cfg"], u.data["o"], u.data["lse"]
+        eo = el = 0.0
+        for (b, h) in heads:
+            q, k, v = (cfg[n][b, h].double().cpu().numpy() for n in ("q", "k", "v"))
+            O, L = attention_head_ref(q, k, v, cfg["scale"], cfg["causal"], query_rows=rows)
+            og = o[b, h].double().cpu().numpy()
+            lg = lse[b, h].double().cpu().numpy()
+            if rows is not None:
+                og, lg = og[rows], lg[rows]
+            eo = max(eo, float(np.abs(og - O).max()))
+            el = max(el, float(np.abs(lg - L).max()))
+        return eo, el
+
+    # cfg3 in full.
+    if "attn_small" in by:
+        u = by["attn_small"]
+        a = u.data["cfg"]["cfg"]
+        eo, el = attn_err(u, [(b, h) for b in range(a["B"]) for h in range(a["H"])])
+        parity["attn_small"] = {"o_max_abs_err": eo, "lse_max_abs_err": el, "o_tol": 2e-2,
+                                "lse_tol": 1e-3, "sample": "every (b, h) and query row"}
+
+    # cfg4: the oracle timed on seeded slices (all query rows of each); the
+    # same slices are compared.
+    if "attn" in by:
+        u = by["attn"]
+        cfg = u.data["cfg"]
+        a = cfg["cfg"]
+        heads = osm_inputs.sample_heads(a["B"], a["H"], a["B"] * a["H"], a["seed"],
+                                        [(0, 0), (7, 39)])
+        done, t_at = [], 0.0
+        for (b, h) in heads:
+            if t_at >= budget_s * 0.2:
+                break
+            q, k, v = (cfg[n][b, h][None, None].double().cpu().numpy() for n in ("q", "k", "v"))
+            t0 = time.perf_counter()
+            attention_ref(q, k, v, cfg["scale"], True)
+            t_at += time.perf_counter() - t0
+            done.append((b, h))
+        pair_flops = 4 * a["D"] * causal_pairs(a["N"], a["causal"])
+        eo, el = attn_err(u, done)
+        cpu["attention"] = {
+            "value": round(pair_flops * len(done) / t_at / 1e12, 6), "unit": "TFLOP/s",
             "cores": blas_threads, "kind": "oracle",
             "sample": (f"float64 materialised-score oracle (numpy + BLAS) on {len(done)} of "
-                       f"{a['B'] * a['H']} (b, h) slices of attn_llama13b ({t_at:.1f} s)")},
-        "attention_backward": {
-            "value": round(bw_flops / t_bw / 1e12, 6), "unit": "TFLOP/s",
+                       f"{a['B'] * a['H']} (b, h) slices of attn_llama13b ({t_at:.1f} s)"),
+            "full_config_s_estimate": round(t_at / len(done) * a["B"] * a["H"], 1),
+            "estimate": "slice time x B*H (extrapolated, not run)"}
+        parity["attn_llama13b"] = {"o_max_abs_err": eo, "lse_max_abs_err": el, "o_tol": 2e-2,
+                                   "lse_tol": 1e-3,
+                                   "sample": f"{len(done)} (b, h) slices incl. (0, 0) and "
+                                             "(7, 39), every query row"}
+
+    # cfg5: one whole head timed (the full-size estimate scales it by B*H);
+    # two heads compared on 1024 seeded query rows each, incl. the last rows.
+    if "attn_long" in by:
+        u = by["attn_long"]
+        cfg = u.data["cfg"]
+        a = cfg["cfg"]
+        q, k, v = (cfg[n][0, 0][None, None].double().cpu().numpy() for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        attention_ref(q, k, v, cfg["scale"], True)
+        t_head = time.perf_counter() - t0
+        pair_flops = 4 * a["D"] * causal_pairs(a["N"], a["causal"])
+        cpu["attention_long"] = {
+            "value": round(pair_flops / t_head / 1e12, 6), "unit": "TFLOP/s",
+            "cores": blas_threads, "kind": "oracle",
+            "sample": f"float64 materialised-score oracle on (b, h) = (0, 0) of attn_long, "
+                      f"all {a['N']} query rows ({t_head:.1f} s)",
+            "full_config_s_estimate": round(t_head * a["B"] * a["H"], 1),
+            "estimate": "head time x B*H (extrapolated, not run)"}
+        g = torch.Generator().manual_seed(a["seed"])
+        rows = sorted(set(torch.randint(0, a["N"], (896,), generator=g).tolist())
+                      | set(range(a["N"] - 128, a["N"])))
+        eo, el = attn_err(u, [(0, 0), (0, a["H"] - 1)], rows)
+        parity["attn_long"] = {"o_max_abs_err": eo, "lse_max_abs_err": el, "o_tol": 2e-2,
+                               "lse_tol": 1e-3,
+                               "sample": f"(b, h) = (0, 0) and (0, {a['H'] - 1}), {len(rows)} "
+                                         "seeded query rows each incl. the last 128"}
+
+    # Backward on cfg4: oracle timed on seeded slices; the library's
+    # gradients compared as max |err| / max(1, max |ref|) per gradient.
+    if "attn_bwd" in by:
+        u = by["attn_bwd"]
+        cfg, do, grads = u.data["cfg"], u.data["do"], u.data["grads"]
+        a = cfg["cfg"]
+        heads = osm_inputs.sample_heads(a["B"], a["H"], a["B"] * a["H"], a["seed"],
+                                        [(0, 0), (7, 39)])
+        done, t_bw, errs = [], 0.0, [0.0, 0.0, 0.0]
+        for (b, h) in heads:
+            if t_bw >= budget_s * 0.2:
+                break
+            q, k, v, dd = (t[b, h].double().cpu().numpy() for t in (cfg["q"], cfg["k"], cfg["v"],
+                                                                      do))
+            t0 = time.perf_counter()
+            refs = attention_bwd_head_ref(q, k, v, dd, cfg["scale"], True)
+            t_bw += time.perf_counter() - t0
+            done.append((b, h))
+            for i, (gt, r) in enumerate(zip(grads, refs)):
+                e = np.abs(gt[b, h].double().cpu().numpy() - r).max() / max(1.0, np.abs(r).max())
+                errs[i] = max(errs[i], float(e))
+        pair_flops = 10 * a["D"] * causal_pairs(a["N"], a["causal"])
+        cpu["attention_backward"] = {
+            "value": round(pair_flops * len(done) / t_bw / 1e12, 6), "unit": "TFLOP/s",
             "cores": blas_threads, "kind": "oracle",
             "sample": (f"float64 softmax-Jacobian gradient oracle (numpy + BLAS) on "
-                       f"{len(done_b)} of {a['B'] * a['H']} (b, h) slices of attn_llama13b "
-                       f"({t_bw:.1f} s); FLOPs counted as the library's five products")},
-    }
+                       f"{len(done)} of {a['B'] * a['H']} (b, h) slices of attn_llama13b "
+                       f"({t_bw:.1f} s); FLOPs counted as the library's five products"),
+            "full_config_s_estimate": round(t_bw / len(done) * a["B"] * a["H"], 1),
+            "estimate": "slice time x B*H (extrapolated, not run)"}
+        parity["attn_llama13b_backward"] = {
+            "dq_scaled_err": errs[0], "dk_scaled_err": errs[1], "dv_scaled_err": errs[2],
+            "measure": "max |gpu - oracle| / max(1, max |oracle|) per gradient",
+            "sample": f"{len(done)} (b, h) slices incl. (0, 0) and (7, 39)"}
+    return cpu, parity
 
 
 class SclkSampler:
@@ -264,38 +433,20 @@ class SclkSampler:
                 "samples": len(busy), "source": "pp_dpm_sclk during the timed steps"}
 
 
-def copy_ceiling(torch, osm_inputs, steps=20):
-    """Device-to-device hipMemcpyAsync of the float32 softmax bytes."""
-    import ctypes
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                   ctypes.c_int, ctypes.c_void_p]
-    x = osm_inputs.softmax_large(device="cuda")
-    y = torch.empty_like(x)
-    nbytes = x.numel() * 4
-    st = torch.cuda.current_stream()
-    def one():
-        # 3 = hipMemcpyDeviceToDevice
-        if hip.hipMemcpyAsync(y.data_ptr(), x.data_ptr(), nbytes, 3, st.cuda_stream) != 0:
-            raise RuntimeError("hipMemcpyAsync failed")
-    for _ in range(3):
-        one()
+def time_launches(torch, stream, launches, steps):
+    """HIP events on `stream` around each launch; `launches` run in turn,
+    `steps` times.  Returns one list of times (ms) per launch."""
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(steps)]
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record(st)
-    for i in range(steps):
-        one()
-        ev[i + 1].record(st)
+    for s in range(steps):
+        for i, f in enumerate(launches):
+            ev[s][i][0].record(stream)
+            f()
+            ev[s][i][1].record(stream)
     torch.cuda.synchronize()
-    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
-    del x, y
-    # A ceiling: the fastest copy, with the median beside it.
-    ms, med = per[0], per[len(per) // 2]
-    return {"GB/s": round(2 * nbytes / ms / 1e6, 1), "ms": round(ms, 5),
-            "median_GB/s": round(2 * nbytes / med / 1e6, 1),
-            "frac_of_hbm_peak": round(2 * nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
-            "method": "hipMemcpyAsync device-to-device, 1 GiB read + 1 GiB written; "
-                      "fastest of the timed copies"}
+    return [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]
+            for i in range(len(launches))]
 
 
 def main():
@@ -303,10 +454,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["softmax_f32", "softmax_bf16", "attn", "attn_bwd",
-                                       "attn_long"], default=None,
-                    help="time one unit (for profiler runs); attn_long runs only here")
-    ap.add_argument("--copy", action="store_true", help="time a plain device copy instead")
+    ap.add_argument("--only", choices=UNIT_NAMES, default=None,
+                    help="time one unit (for profiler runs)")
+    ap.add_argument("--copy", action="store_true", help="time a plain runtime device copy instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     args = ap.parse_args()
@@ -374,17 +524,17 @@ def main():
     for s in range(args.steps):
         for i, u in enumerate(units):
             u.times_ms.append(marks[s][i][0].elapsed_time(marks[s][i][1]))
-    # Units outside the step: their own loop, the same number of launches.
+    # Units outside the step: their own loop, the same number of launches; a
+    # unit with a partner alternates with it launch by launch.
+    by = {u.name: u for u in all_units}
+    paired = {}
     for u in extra:
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for e0, e1 in ev:
-            e0.record(stream)
-            u.launch()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        u.times_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+        if u.pair in by:
+            p = by[u.pair]
+            t_u, t_p = time_launches(torch, stream, [u.launch, p.launch], args.steps)
+            u.times_ms, paired[p.name] = t_u, t_p
+        else:
+            u.times_ms = time_launches(torch, stream, [u.launch], args.steps)[0]
 
     traffic = read_traffic()
     rooflines = []
@@ -396,25 +546,27 @@ def main():
         tr_bytes = None
         if tr and tr.get("src") == kernel_source_hash(u.src):
             tr_bytes = int(float(tr["fetch_bytes"])) + int(float(tr["write_bytes"]))
-        rooflines.append({
+        r = {
             "unit_name": u.name, "kernel": u.kernel, "workload": u.workload,
             "bound": u.bound, "achieved": round(achieved, 2), "peak": u.peak, "unit": u.unit,
             "frac": round(achieved / u.peak, 4), "traffic": tr_bytes,
             "algorithmic": u.work, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5),
             "min_ms": round(min(u.times_ms), 5), "max_ms": round(max(u.times_ms), 5),
-            "in_step": u.in_step})
+            "in_step": u.in_step}
+        if u.note:
+            r["note"] = u.note
+        rooflines.append(r)
     in_step = [r for r in rooflines if r["in_step"]] or rooflines
     dominant = max(in_step, key=lambda r: r["avg_ms"])
+    rl = {r["unit_name"]: r for r in rooflines}
 
-    sm = [r for r in rooflines if r["unit_name"].startswith("softmax")]
-    at = [r for r in rooflines if r["unit_name"] == "attn"]
-    bw = [r for r in rooflines if r["unit_name"] == "attn_bwd"]
+    sm = [r for r in rooflines if r["unit_name"] in ("softmax_f32", "softmax_bf16")]
     if sm:
         sm_bytes = sum(r["algorithmic"] for r in sm)
         sm_ms = sum(r["avg_ms"] for r in sm)
         value, unit = sm_bytes / (sm_ms * 1e-3) / 1e9, "GB/s"
     else:
-        first = (at or bw or rooflines)[0]
+        first = rooflines[0]
         value, unit = first["achieved"], first["unit"]
 
     result = {
@@ -442,24 +594,34 @@ def main():
                                               "traffic")} | {"kernel": dominant["kernel"]},
         "rooflines": rooflines,
     }
-    if at:
-        result["attention"] = {"value": at[0]["achieved"], "unit": "TFLOP/s",
-                               "frac_of_bf16_peak": at[0]["frac"],
+    if "attn" in rl:
+        result["attention"] = {"value": rl["attn"]["achieved"], "unit": "TFLOP/s",
+                               "frac_of_bf16_peak": rl["attn"]["frac"],
                                "flop_convention": "4*D per unmasked (query, key) pair"}
-    if bw:
+    if "attn_bwd" in rl:
         result["attention_backward"] = {
-            "value": bw[0]["achieved"], "unit": "TFLOP/s", "frac_of_bf16_peak": bw[0]["frac"],
-            "avg_ms": bw[0]["avg_ms"], "in_step": False,
+            "value": rl["attn_bwd"]["achieved"], "unit": "TFLOP/s",
+            "frac_of_bf16_peak": rl["attn_bwd"]["frac"], "avg_ms": rl["attn_bwd"]["avg_ms"],
+            "in_step": False,
             "flop_convention": "10*D per unmasked (query, key) pair (five products)"}
+    if "copy_f32" in rl and "softmax_f32" in paired:
+        t_sm = paired["softmax_f32"]
+        sm_avg = sum(t_sm) / len(t_sm)
+        cp = rl["copy_f32"]
+        sm_gbs = rl["softmax_f32"]["algorithmic"] / (sm_avg * 1e-3) / 1e9
+        result["copy_ceiling"] = {
+            "GB/s": cp["achieved"], "frac_of_hbm_peak": cp["frac"], "avg_ms": cp["avg_ms"],
+            "softmax_f32_interleaved_GB/s": round(sm_gbs, 2),
+            "softmax_f32_frac_of_copy": round(sm_gbs / cp["achieved"], 4),
+            "method": ("osm_stream_copy (16-byte non-temporal loads and stores, the softmax's "
+                       "access pattern) on the 1 GiB fp32 softmax input, 1 GiB read + 1 GiB "
+                       "written, alternated launch by launch with the fp32 softmax")}
     result["sclk_mhz"] = sclk.summary()
-    if args.only is None:
-        cc = copy_ceiling(torch, osm_inputs)
-        if sm:
-            cc["softmax_frac_of_copy"] = round(value / cc["GB/s"], 4)
-        result["copy_ceiling"] = cc
     if not args.no_cpu_baseline and args.only is None:
-        result["cpu_baseline"] = cpu_baseline(torch, osm_inputs, args.cpu_budget)
-        result["cpu_baseline"]["host_cpus"] = len(os.sched_getaffinity(0))
+        cpu, parity = oracle_leg(torch, osm_inputs, all_units, args.cpu_budget)
+        cpu["host_cpus"] = len(os.sched_getaffinity(0))
+        result["cpu_baseline"] = cpu
+        result["parity"] = parity
     print(json.dumps(result), flush=True)
 
 

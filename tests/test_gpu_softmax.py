@@ -1,7 +1,7 @@
 """GPU parity tests of osm_softmax_rows against the float64 CPU oracle.
 
 Tolerances: float32 output, max |gpu - oracle| <= 1e-6; bfloat16 output,
-|gpu - oracle| <= half a bfloat16 ulp of the oracle value plus 2^-16 relative
+|gpu - oracle| <= half a bfloat16 ulp of the oracle value plus 2^-15 relative
 (round to nearest even meets it, truncation does not: tests/tolerance.py);
 -inf inputs give exact zeros, and all -inf rows give all zeros.  Every call
 goes through the C ABI.

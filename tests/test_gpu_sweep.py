@@ -7,7 +7,7 @@ mask and split-K in one call; the backward with key lengths at ragged sizes;
 the softmax with masks, row lengths and the split-row kernels.  The
 tolerances are those of the other GPU tests (the helpers are imported from
 them): attention O 2e-2 and LSE 1e-3, the backward's scaled bound, float32
-softmax 1e-6 and bfloat16 softmax half an ulp plus 2^-16 relative.
+softmax 1e-6 and bfloat16 softmax half an ulp plus 2^-15 relative.
 """
 
 import math

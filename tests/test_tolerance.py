@@ -52,11 +52,11 @@ def test_softmax_bound_accepts_nearest_even_and_rejects_truncation():
 
 
 def test_float32_error_inside_the_slack_passes():
-    # A float32 result a few float32 ulps off, then rounded to nearest even,
-    # stays inside the bound (the slack is 2^-16 relative, float32 has 2^-24).
+    # A float32 result up to 2^-17 off, then rounded to nearest even, stays
+    # inside the bound (the slack is 2^-15 relative).
     rng = np.random.default_rng(3)
     ref = np.exp(rng.uniform(-60, 0, 200000))
-    noisy = ref * (1 + rng.uniform(-2.0 ** -18, 2.0 ** -18, ref.shape))
+    noisy = ref * (1 + rng.uniform(-2.0 ** -17, 2.0 ** -17, ref.shape))
     assert not bf16_rne_violations(_rne(noisy), ref).any()
 
 
