@@ -276,14 +276,33 @@ __device__ __forceinline__ void acc_products(const char* t1, const char* t2,
   }
 }
 
-// Map a linear workgroup id to (batch*head, block).  Workgroups go
-// round-robin over the 8 XCDs; when B*H is a multiple of 8, all blocks of one
-// head land on one XCD, whose L2 then holds the head's streamed tiles.
+// Map a linear workgroup id to (batch*head, block rank); rank 0 is the
+// heaviest block under the causal mask.  Workgroups go round-robin over the 8
+// XCDs; when B*H is a multiple of 8, the heads an XCD owns are those with
+// bh mod 8 equal to it, so its L2 holds their streamed tiles.
+//   kCausal: rank-major, every head's rank-0 block before any rank-1 block,
+//            and so on: blocks are dispatched heaviest first over the whole
+//            launch, so no heavy block starts late and sets its end.
+//   otherwise: head-major, all blocks of a head together (equal work; the
+//            fewest heads in flight per XCD).
+// Measured at B8 H40 N2048 (interleaved): rank-major is 13% faster than
+// head-major for causal D = 64 and level to 3% faster at D = 128, but 13%
+// slower without the mask, where only L2 reuse differs.
+template <bool kCausal>
 __device__ __forceinline__ void block_of(int L, int per_head, int BH, int& bh, int& rank) {
   if ((BH & 7) == 0) {
     const int xcd = L & 7, idx = L >> 3;
-    bh = (idx / per_head) * 8 + xcd;
-    rank = idx % per_head;
+    const int hpx = BH >> 3;
+    if constexpr (kCausal) {
+      bh = (idx % hpx) * 8 + xcd;
+      rank = idx / hpx;
+    } else {
+      bh = (idx / per_head) * 8 + xcd;
+      rank = idx % per_head;
+    }
+  } else if constexpr (kCausal) {
+    bh = L % BH;
+    rank = L / BH;
   } else {
     bh = L / per_head;
     rank = L % per_head;
@@ -325,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(
   const int col = lane & 31, half = lane >> 5;
   const int nkb = (N + kBlk - 1) / kBlk;
   int bh, kb;
-  block_of(blockIdx.x, nkb, BH, bh, kb);  // causal: the heaviest blocks (kb = 0) first
+  block_of<kCausal>(blockIdx.x, nkb, BH, bh, kb);  // causal: kb = rank, the heaviest first
   const int64_t head = (int64_t)bh * N * D;
   const int head_bytes = N * D * 2;
   const int kw = kb * kBlk + wave * 32;  // first key of this wave
@@ -515,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   const int col = lane & 31, half = lane >> 5;
   const int nqb = (N + kBlk - 1) / kBlk;
   int bh, rank;
-  block_of(blockIdx.x, nqb, BH, bh, rank);
+  block_of<kCausal>(blockIdx.x, nqb, BH, bh, rank);
   const int qt = kCausal ? nqb - 1 - rank : rank;  // causal: the heaviest blocks first
   const int64_t head = (int64_t)bh * N * D;
   const int head_bytes = N * D * 2;
