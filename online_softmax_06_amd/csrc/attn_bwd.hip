@@ -280,29 +280,41 @@ __device__ __forceinline__ void acc_products(const char* t1, const char* t2,
 // heaviest block under the causal mask.  Workgroups go round-robin over the 8
 // XCDs; when B*H is a multiple of 8, the heads an XCD owns are those with
 // bh mod 8 equal to it, so its L2 holds their streamed tiles.
-//   kCausal: rank-major, every head's rank-0 block before any rank-1 block,
-//            and so on: blocks are dispatched heaviest first over the whole
-//            launch, so no heavy block starts late and sets its end.
+//   kCausal: the heads of an XCD in groups of kGroup; within a group
+//            rank-major (every head's rank-0 block, then every rank-1
+//            block, ...), groups in order.  Heavy blocks then start first
+//            and no heavy block is dispatched late to set the end of the
+//            launch, while an XCD still streams the tiles of few heads at a
+//            time.
 //   otherwise: head-major, all blocks of a head together (equal work; the
 //            fewest heads in flight per XCD).
-// Measured at B8 H40 N2048 (interleaved): rank-major is 13% faster than
-// head-major for causal D = 64 and level to 3% faster at D = 128, but 13%
-// slower without the mask, where only L2 reuse differs.
+// Measured interleaved, causal D = 128: B8 H40 N2048 1136 us against 1246
+// us head-major and 1183 us rank-major over all of an XCD's heads (which
+// also fetched 3.4x the bytes from beyond L2); B16 H40 N1024 +11%,
+// B8 H40 N2048 D = 64 +6%.  Without the mask, head-major is fastest.
+constexpr int kGroup = 8;
+
 template <bool kCausal>
 __device__ __forceinline__ void block_of(int L, int per_head, int BH, int& bh, int& rank) {
   if ((BH & 7) == 0) {
     const int xcd = L & 7, idx = L >> 3;
     const int hpx = BH >> 3;
     if constexpr (kCausal) {
-      bh = (idx % hpx) * 8 + xcd;
-      rank = idx / hpx;
+      const int grp = idx / (kGroup * per_head);
+      const int gsz = min(kGroup, hpx - grp * kGroup);  // heads in this group
+      const int r = idx - grp * kGroup * per_head;
+      bh = (grp * kGroup + r % gsz) * 8 + xcd;
+      rank = r / gsz;
     } else {
       bh = (idx / per_head) * 8 + xcd;
       rank = idx % per_head;
     }
   } else if constexpr (kCausal) {
-    bh = L % BH;
-    rank = L / BH;
+    const int grp = L / (kGroup * per_head);
+    const int gsz = min(kGroup, BH - grp * kGroup);
+    const int r = L - grp * kGroup * per_head;
+    bh = grp * kGroup + r % gsz;
+    rank = r / gsz;
   } else {
     bh = L / per_head;
     rank = L % per_head;
