@@ -224,11 +224,16 @@ def oracle_leg(torch, osm_inputs, units, budget_s):
 
     # cfg1: the three small calls in full.
     if "softmax_small" in by:
-        err = 0.0
+        err, t_o = 0.0, 0.0
         for label, x, y in by["softmax_small"].data["calls"]:
-            ref = softmax_rows_ref(x.double().cpu().numpy())
+            xs = x.double().cpu().numpy()
+            t0 = time.perf_counter()
+            ref = softmax_rows_ref(xs)
+            t_o += time.perf_counter() - t0
             err = max(err, float(np.abs(y.double().cpu().numpy() - ref).max()))
         parity["softmax_small"] = {"max_abs_err": err, "tol": 1e-6, "sample": "all three calls"}
+        cpu["softmax_small"] = {"seconds": round(t_o, 5), "cores": 1, "kind": "oracle",
+                                "sample": "all three calls, in full"}
 
     # cfg2, float32: the oracle timed on whole 1024-row chunks, and compared.
     c = osm_inputs.SOFTMAX_LARGE
@@ -260,18 +265,24 @@ def oracle_leg(torch, osm_inputs, units, budget_s):
         ref = softmax_rows_ref(x[rows].double().cpu().numpy())
         got = y[rows].double().cpu().numpy()
         e = np.abs(got - ref)
+        cpu["softmax_large_bf16_sample"] = {
+            "note": "the bf16 run's oracle is the fp32 run's oracle on bf16-rounded inputs; "
+                    "its rate is the fp32 figure above"}
         parity["softmax_large_bf16"] = {
             "max_abs_err": float(e.max()),
             "max_err_over_rne_bound": float((e / _rne_bound(ref)).max()),
             "tol": "half a bf16 ulp + 2^-15 relative (ratio <= 1)",
             "sample": "1024 seeded rows incl. the first and last"}
 
-    def attn_err(u, heads, rows=None):
+    def attn_err(u, heads, rows=None, clock=None):
         cfg, o, lse = u.data["cfg"], u.data["o"], u.data["lse"]
         eo = el = 0.0
         for (b, h) in heads:
             q, k, v = (cfg[n][b, h].double().cpu().numpy() for n in ("q", "k", "v"))
+            t0 = time.perf_counter()
             O, L = attention_head_ref(q, k, v, cfg["scale"], cfg["causal"], query_rows=rows)
+            if clock is not None:
+                clock[0] += time.perf_counter() - t0
             og = o[b, h].double().cpu().numpy()
             lg = lse[b, h].double().cpu().numpy()
             if rows is not None:
@@ -284,9 +295,12 @@ def oracle_leg(torch, osm_inputs, units, budget_s):
     if "attn_small" in by:
         u = by["attn_small"]
         a = u.data["cfg"]["cfg"]
-        eo, el = attn_err(u, [(b, h) for b in range(a["B"]) for h in range(a["H"])])
+        clock = [0.0]
+        eo, el = attn_err(u, [(b, h) for b in range(a["B"]) for h in range(a["H"])], clock=clock)
         parity["attn_small"] = {"o_max_abs_err": eo, "lse_max_abs_err": el, "o_tol": 2e-2,
                                 "lse_tol": 1e-3, "sample": "every (b, h) and query row"}
+        cpu["attn_small"] = {"seconds": round(clock[0], 4), "cores": blas_threads, "kind": "oracle",
+                             "sample": "every (b, h) and query row, in full"}
 
     # cfg4: the oracle timed on seeded slices (all query rows of each); the
     # same slices are compared.
