@@ -520,8 +520,9 @@ __device__ __forceinline__ void tail_sub_step(WaveState<D>& st, const char* kslo
 }
 
 // Which (head, query tile) items a workgroup processes.
-//   kOnePerGroup: item = the workgroup's own id (split-K launches: one item
-//                 per workgroup, mapped by tile_of / tile_of_split).
+//   kOnePerGroup: item = the workgroup's own id, mapped by tile_of /
+//                 tile_of_split (split-K launches, and grids with no more
+//                 query tiles than resident workgroups).
 //   kPairsXcd:    a persistent grid, `workers` workgroups per XCD.  Items are
 //                 folded in pairs (query tiles p and nqt - 1 - p of one head,
 //                 so with a causal mask every pair holds the same number of
@@ -892,7 +893,15 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   } else {
     // Resident workgroups: per_cu() per compute unit.
     const int slots = per_cu<D, kW, kBias, kSplit>() * device_cus();
-    if ((BH & 7) == 0 && slots >= 8) {
+    const int64_t items = (int64_t)nqt * BH;
+    if (items <= slots) {
+      // Small grid: every query tile gets a workgroup of its own (heaviest
+      // first when causal); folding pairs would run two tiles back to back
+      // while compute units stay idle.
+      sc.mode = kOnePerGroup;
+      sc.workers = 0;
+      grid = items;
+    } else if ((BH & 7) == 0 && slots >= 8) {
       sc.mode = kPairsXcd;
       const int64_t per_xcd = (int64_t)sc.heads_per_xcd * sc.pairs;
       sc.workers = (int)(per_xcd < slots / 8 ? per_xcd : slots / 8);
@@ -930,13 +939,16 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
                                                       splits, o_part, lse_part, s);
   }
   // Eight wavefronts for rows without a causal diagonal or with many key
-  // tiles per diagonal (the crossover measured at N = 4096).
+  // tiles per diagonal (the crossover measured at N = 4096), when their
+  // 256-row tiles still give every compute unit one (else the 128-row tiles
+  // of four wavefronts spread the work over twice as many workgroups).
   if constexpr (D == 128 && !kSplit) {
-    if (!causal) {
+    const bool fills = (int64_t)((N + 255) / 256) * BH >= device_cus();
+    if (!causal && fills) {
       return launch<D, 8, false, false, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
                                                 o_part, lse_part, s);
     }
-    if (N >= 4096) {
+    if (causal && fills && N >= 4096) {
       return launch<D, 8, true, false, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
                                                o_part, lse_part, s);
     }
