@@ -14,7 +14,7 @@ import torch
 
 import online_softmax_06_amd as osm
 import osm_inputs
-from oracle import attention_ref
+from oracle import attention_head_ref, attention_ref
 from tolerance import CONSTANT_V_MIN_KEYS, O_ABS_SLACK, bf16_rne_violations
 
 pytestmark = pytest.mark.gpu
@@ -66,8 +66,7 @@ ODD = [
     (1, 2, 255, 64), (1, 1, 1000, 64),
     (1, 1, 1, 128), (1, 2, 17, 128), (2, 1, 64, 128), (1, 3, 100, 128), (1, 1, 129, 128),
     (1, 2, 255, 128), (1, 1, 1000, 128), (1, 1, 2049, 128),
-    # Causal rows this long take the 8-wavefront workgroups (as unmasked
-    # rows of any length at D = 128 do); a ragged tail past 4096.
+    # A ragged tail past 4096 (at this grid size still 128-row tiles).
     (1, 2, 4100, 128),
 ]
 
@@ -82,6 +81,44 @@ def test_odd_shapes_full(B, H, N, D, causal):
     o, lse = osm.attn_fwd(q, k, v, scale, causal)
     torch.cuda.synchronize()
     compare(q, k, v, scale, causal, o, lse)
+
+
+# Grids with more query tiles than resident workgroups (MI355X: 256 compute
+# units; 512 slots for 128-row tiles at D = 128, 768 at D = 64, 256 for the
+# 256-row tiles of 8 wavefronts) run the persistent schedule: query tiles
+# folded in pairs (p, n - 1 - p), the middle tile alone when n is odd, dealt
+# over the heads of an XCD when B * H is a multiple of 8, else over all heads.
+PAIR_GRIDS = [
+    (8, 40, 1920, 128, True),   # heads per XCD, 15 tiles of 128 rows
+    (4, 50, 1152, 64, True),    # heads per XCD, D = 64, 9 tiles
+    (3, 67, 1152, 64, True),    # B * H = 201: all heads
+    (3, 3, 7900, 128, True),    # all heads, 8 wavefronts, 31 tiles, ragged
+    (3, 3, 8100, 128, False),   # all heads, 8 wavefronts, unmasked, ragged
+    (2, 8, 4200, 128, False),   # heads per XCD, 8 wavefronts, 17 tiles, ragged
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,causal", PAIR_GRIDS)
+def test_pair_schedules_sampled(B, H, N, D, causal):
+    _announce("pairs", B, H, N, D, causal)
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=N + H, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o, lse = osm.attn_fwd(q, k, v, scale, causal)
+    torch.cuda.synchronize()
+    rows_per_tile = 256 if (D == 128 and (not causal or N >= 4096)) else 128
+    n_tiles = (N + rows_per_tile - 1) // rows_per_tile
+    mid = (n_tiles // 2) * rows_per_tile
+    rng = np.random.default_rng(N * 7 + H)
+    rows = set(rng.choice(N, 96, replace=False).tolist())
+    rows |= {0, 1, mid, mid + rows_per_tile // 2, min(mid + rows_per_tile, N) - 1}
+    rows |= set(range(N - 8, N))
+    rows = sorted(rows)
+    for b, h in osm_inputs.sample_heads(B, H, 3, N, must=[(0, 0), (B - 1, H - 1)]):
+        qh, kh, vh = (t[b, h].cpu().double().numpy() for t in (q, k, v))
+        O, L = attention_head_ref(qh, kh, vh, scale, causal, query_rows=rows)
+        eo = np.abs(o[b, h].cpu().double().numpy()[rows] - O).max()
+        el = np.abs(lse[b, h].cpu().double().numpy()[rows] - L).max()
+        assert eo <= O_TOL and el <= LSE_TOL, ((b, h), eo, el)
 
 
 @pytest.mark.parametrize("D", [64, 128])
