@@ -70,7 +70,8 @@ constexpr float kLag = 8.0f;  // allowed lag of the exponent reference (log2 uni
 // wavefronts of a SIMD advance together and every K/V tile in LDS serves
 // twice the rows.  Its 256-row query tiles cost more on the causal diagonal,
 // where a wavefront idles over the sub-tiles above its rows, so the launch
-// takes kW = 8 for long or unmasked rows and kW = 4 for short causal rows.
+// takes kW = 8 for long or unmasked rows (when its tiles fill the compute
+// units) and kW = 4 for short causal rows and small grids.
 template <int D, int kW>
 struct Shape {
   static_assert(kW == 4 || (kW == 8 && D == 128), "supported shapes");
