@@ -64,10 +64,17 @@ UNIT_NAMES = ["softmax_f32", "softmax_bf16", "attn", "attn_bwd", "attn_long", "a
 
 
 def kernel_source_hash(fname):
+    """Hash of a kernel's code: its source file and osm_device.h with the
+    comments and blank lines taken out, so that counters stay attached to a
+    kernel whose comments alone changed."""
     h = hashlib.sha256()
     for f in (fname, "osm_device.h"):
-        with open(os.path.join(SRC_DIR, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(SRC_DIR, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 
