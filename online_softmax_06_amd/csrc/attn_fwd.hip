@@ -709,6 +709,27 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
     __syncthreads();
     if (sw_last >= s0) st.sc = sub_scores<D>((j_begin & 1) ? ks2 : ks0, off, st.qreg);
 
+    int full_end = min(j_end, kvlen / kBN);
+    if constexpr (kCausal) full_end = min(full_end, q0 / kBN);
+    const int main_end = max(j_begin, min(full_end, j_end - 1));
+    if constexpr (!kBias) {
+      // When the item starts with an unmasked tile, its first sub-tile's row
+      // max becomes the exponent reference: the first sub-step then forms P
+      // once, instead of taking the re-reference branch that a reference of
+      // -inf forces (a second round of exponentials and a rescale of the
+      // empty accumulator).  With a bias the scores are complete only inside
+      // the sub-step, which keeps the branch.
+      if (main_end > j_begin) {
+        const f32x16& sc = st.sc;
+        float mx = max3(sc[0], sc[1], sc[2]);
+#pragma unroll
+        for (int i = 3; i < 15; i += 2) mx = max3(mx, sc[i], sc[i + 1]);
+        mx = __builtin_fmaxf(mx, sc[15]);
+        mx = __builtin_fmaxf(mx, swap_halves(mx));
+        st.m_run = mx * scale_log2;
+      }
+    }
+
     // A2: at the top of the step for tile j, K sub-tiles 2j + 1 and 2j + 2
     // and V_j have landed and every wave is done with sub-tiles 2j - 1 and 2j
     // and with V_{j-1}, whose places receive sub-tiles 2j + 3, 2j + 4 (copied
@@ -756,9 +777,6 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
                                         scale_log2, brow, opt, cp1);                          \
   } while (0)
 
-    int full_end = min(j_end, kvlen / kBN);
-    if constexpr (kCausal) full_end = min(full_end, q0 / kBN);
-    const int main_end = max(j_begin, min(full_end, j_end - 1));
     int j = j_begin;
     if ((j & 1) && j < main_end) {
       OSM_MAIN_TILE(j, true);
