@@ -10,8 +10,11 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE memory owned by the caller.  The library
- *     allocates nothing, frees nothing and keeps no state between calls; calls
- *     from several host threads are safe.
+ *     allocates nothing and frees nothing.  Between calls it keeps only
+ *     per-device facts it looks up once (the compute-unit count, the address
+ *     of osm_attn_bwd_noalloc's fixed scratch array) and that array's
+ *     content.  Calls from several host threads are safe, except overlapping
+ *     osm_attn_bwd_noalloc calls on one GPU (see there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
  *     the call returns without waiting.  The caller synchronises.
  *   - Arguments are validated on the host before any HIP call.  An invalid call
