@@ -499,27 +499,6 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
   if constexpr (kNext) st.sc = sn;
 }
 
-// A sub-step of the last key tiles: skipped past the wave's last visible
-// sub-tile, always masked (these sub-tiles may cross the causal diagonal or
-// the key length).  It always forms the next scores, also on the wave's last
-// sub-tile, where they are not used: one code path keeps the register
-// allocation of the tail as simple as that of the main loop.
-template <int D, bool kCausal, int kKb, bool kBias, typename Copy>
-__device__ __forceinline__ void tail_sub_step(WaveState<D>& st, const char* kslot_next,
-                                              const char* vtile, const LaneOffsets<D>& off,
-                                              int s, int sw_last, int N, int kvlen, int qrow,
-                                              int half, float scale_log2, const float* brow,
-                                              const AttnOptions& opt, const Copy& copy) {
-  if (s > sw_last) {
-    // The wave still issues its share of the copies.
-#pragma unroll
-    for (int i = 0; i < D / 16 - 1; ++i) copy(i);
-    return;
-  }
-  sub_step<D, kCausal, kKb, true, true, kBias>(st, kslot_next, vtile, off, s, N, kvlen, qrow, half,
-                                               scale_log2, brow, opt, copy);
-}
-
 // Which (head, query tile) items a workgroup processes.
 //   kOnePerGroup: item = the workgroup's own id, mapped by tile_of /
 //                 tile_of_split (split-K launches, and grids with no more
@@ -763,18 +742,46 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
                                                 scale_log2, brow, opt, cp1);                  \
   } while (0)
     // The last tiles (those crossing the diagonal or the key length, and the
-    // final one), with per-wave choices.
-#define OSM_TAIL_TILE(J, ODD)                                                                 \
+    // final one): always masked, and per wave in three wave-uniform runs --
+    // tiles whose two sub-tiles the wave computes (up to its last visible
+    // sub-tile sw_last), at most one tile whose first sub-tile only it
+    // computes, then tiles where it only issues its share of the copies.
+    // Every tile still has its one barrier for every wave.  With a branch per
+    // sub-tile instead, the compiler gave the two paths different register
+    // assignments and copied 64-80 VGPRs at every join.  A masked sub-step
+    // always forms the next scores, also on the wave's last sub-tile, where
+    // they are not used: one code path for every computed sub-tile.
+#define OSM_TAIL_FULL(J, ODD)                                                                 \
   do {                                                                                        \
     __builtin_amdgcn_s_waitcnt(0);                                                            \
     __syncthreads();                                                                          \
     OSM_TILE_COPIES(J, ODD);                                                                  \
-    tail_sub_step<D, kCausal, 0, kBias>(st, ODD ? ks3 : ks1, ODD ? vb1 : vb0, off, 2 * (J),   \
-                                        sw_last, N, kvlen, qrow, half, scale_log2, brow, opt, \
-                                        cp0);                                                 \
-    tail_sub_step<D, kCausal, 1, kBias>(st, ODD ? ks0 : ks2, ODD ? vb1 : vb0, off,            \
-                                        2 * (J) + 1, sw_last, N, kvlen, qrow, half,           \
-                                        scale_log2, brow, opt, cp1);                          \
+    sub_step<D, kCausal, 0, true, true, kBias>(st, ODD ? ks3 : ks1, ODD ? vb1 : vb0, off,     \
+                                               2 * (J), N, kvlen, qrow, half, scale_log2,     \
+                                               brow, opt, cp0);                               \
+    sub_step<D, kCausal, 1, true, true, kBias>(st, ODD ? ks0 : ks2, ODD ? vb1 : vb0, off,     \
+                                               2 * (J) + 1, N, kvlen, qrow, half,             \
+                                               scale_log2, brow, opt, cp1);                   \
+  } while (0)
+#define OSM_TAIL_HALF(J, ODD)                                                                 \
+  do {                                                                                        \
+    __builtin_amdgcn_s_waitcnt(0);                                                            \
+    __syncthreads();                                                                          \
+    OSM_TILE_COPIES(J, ODD);                                                                  \
+    sub_step<D, kCausal, 0, true, true, kBias>(st, ODD ? ks3 : ks1, ODD ? vb1 : vb0, off,     \
+                                               2 * (J), N, kvlen, qrow, half, scale_log2,     \
+                                               brow, opt, cp0);                               \
+    _Pragma("unroll") for (int i = 0; i < kDC - 1; ++i) cp1(i);                               \
+  } while (0)
+#define OSM_TAIL_EMPTY(J, ODD)                                                                \
+  do {                                                                                        \
+    __builtin_amdgcn_s_waitcnt(0);                                                            \
+    __syncthreads();                                                                          \
+    OSM_TILE_COPIES(J, ODD);                                                                  \
+    _Pragma("unroll") for (int i = 0; i < kDC - 1; ++i) {                                     \
+      cp0(i);                                                                                 \
+      cp1(i);                                                                                 \
+    }                                                                                         \
   } while (0)
 
     int j = j_begin;
@@ -790,14 +797,46 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
       OSM_MAIN_TILE(j, false);
       ++j;
     }
-    for (; j < j_end; ++j) {
-      if (j & 1) {
-        OSM_TAIL_TILE(j, true);
-      } else {
-        OSM_TAIL_TILE(j, false);
-      }
+    // Tail tiles j with 2j + 1 <= sw_last: both sub-tiles computed.
+    int tail_full = min(j_end, (sw_last + 1) / 2);
+    tail_full = max(tail_full, j);
+    if ((j & 1) && j < tail_full) {
+      OSM_TAIL_FULL(j, true);
+      ++j;
     }
-#undef OSM_TAIL_TILE
+    for (; j + 1 < tail_full; j += 2) {
+      OSM_TAIL_FULL(j, false);
+      OSM_TAIL_FULL(j + 1, true);
+    }
+    if (j < tail_full) {
+      OSM_TAIL_FULL(j, false);
+      ++j;
+    }
+    // The tile holding sw_last as its first sub-tile.
+    if (j < j_end && 2 * j == sw_last) {
+      if (j & 1) {
+        OSM_TAIL_HALF(j, true);
+      } else {
+        OSM_TAIL_HALF(j, false);
+      }
+      ++j;
+    }
+    // Tiles past the wave's last visible sub-tile: copies only.
+    if ((j & 1) && j < j_end) {
+      OSM_TAIL_EMPTY(j, true);
+      ++j;
+    }
+    for (; j + 1 < j_end; j += 2) {
+      OSM_TAIL_EMPTY(j, false);
+      OSM_TAIL_EMPTY(j + 1, true);
+    }
+    if (j < j_end) {
+      OSM_TAIL_EMPTY(j, false);
+      ++j;
+    }
+#undef OSM_TAIL_EMPTY
+#undef OSM_TAIL_HALF
+#undef OSM_TAIL_FULL
 #undef OSM_MAIN_TILE
 #undef OSM_TILE_COPIES
     // The last tile's copies (zero fills of slots past the item) land before
