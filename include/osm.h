@@ -11,10 +11,16 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE memory owned by the caller.  The library
  *     allocates nothing and frees nothing.  Between calls it keeps only
- *     per-device facts it looks up once (the compute-unit count, the address
- *     of osm_attn_bwd_noalloc's fixed scratch array) and that array's
+ *     per-device facts it looks up once (the compute-unit count, the
+ *     addresses of two fixed device arrays: osm_attn_bwd_noalloc's scratch
+ *     and the attention forward's work-queue counters) and those arrays'
  *     content.  Calls from several host threads are safe, except overlapping
  *     osm_attn_bwd_noalloc calls on one GPU (see there).
+ *   - The attention forward hands out its work through 64 queue slots per
+ *     GPU, one per launch in turn, each reset by the launch that used it: at
+ *     most 64 forward launches may run at the same time on one GPU.  A
+ *     launch captured in a HIP graph keeps its slot, so replays of one graph
+ *     must not run concurrently with each other.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
  *     the call returns without waiting.  The caller synchronises.
  *   - Arguments are validated on the host before any HIP call.  An invalid call
@@ -23,6 +29,8 @@
  *     printed and nothing aborts.
  *   - Results are deterministic: reductions use a fixed order and no atomics,
  *     so the same inputs give bitwise-identical outputs on the same device.
+ *     (The forward's queue counters only decide which workgroup computes an
+ *     item, never how.)
  */
 #ifndef OSM_H_
 #define OSM_H_

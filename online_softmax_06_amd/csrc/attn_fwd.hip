@@ -47,9 +47,17 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "osm_device.h"
 #include "osm_internal.h"
+
+// Work queues of the persistent forward launches: per launch slot, one claim
+// counter per XCD partition (8) and one exit counter per partition (8).
+// Launches take slots in turn; the last workgroup of a partition to leave
+// resets both of its counters, so every launch finds its slot at zero.
+constexpr int kQueueSlots = 64;
+static __device__ unsigned fwd_queue[kQueueSlots * 16];
 
 namespace osm {
 namespace {
@@ -513,15 +521,47 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
 //                 workgroup waits to be dispatched behind a longer one.
 //   kPairsAll:    the same over all heads and the whole grid (B * H not a
 //                 multiple of 8).
-enum : int { kOnePerGroup = 0, kPairsXcd = 1, kPairsAll = 2 };
+//   kQueue:       a persistent grid whose workgroups claim items one at a
+//                 time from an atomic counter of their partition (the heads
+//                 bh = x mod 8 for workgroups x mod 8, or all heads), in the
+//                 order of queue_item.  With two or three workgroups per CU
+//                 the first dispatched one gets the larger share of the
+//                 SIMDs; with a fixed share of items each, the other then
+//                 finished its last items alone, one wavefront per SIMD, for
+//                 about a fifth of the launch.  Claiming lets the faster one
+//                 take more items.  Used for 4-wavefront launches without a
+//                 bias; with one 8-wavefront workgroup per CU kPairsXcd keeps
+//                 fewer heads in flight per L2 and is faster, and so it is
+//                 with a bias (whose score tiles the pairs also share).
+enum : int { kOnePerGroup = 0, kPairsXcd = 1, kPairsAll = 2, kQueue = 3 };
 
 struct Schedule {
   int mode;
   int nqt;            // query tiles per head
   int pairs;          // pairs per head: ceil(nqt / 2)
   int heads_per_xcd;  // kPairsXcd: B * H / 8
-  int workers;        // kPairsXcd: workgroups per XCD; kPairsAll: grid size
+  int workers;        // kPairsXcd: workgroups per XCD; kPairsAll: grid size;
+                      // kQueue: workgroups per partition
+  int parts;          // kQueue: partitions (8 when B * H is a multiple of 8, else 1)
+  int heads;          // kQueue: heads per partition
+  int group;          // kQueue: heads visited together
+  int total;          // kQueue: items per partition
 };
+
+// kQueue: item `idx` of partition `part`.  The heads of a partition (bh =
+// part mod parts) are visited in groups of `group`; inside a group the
+// query tiles go rank-major (every head's heaviest tile, then every head's
+// next, ...), so a group's heads share the L2 and the lightest tiles come
+// last, where they even out the end of the launch.
+__device__ __forceinline__ void queue_item(const Schedule& sc, int idx, int part, bool causal,
+                                           int& bh, int& qt) {
+  const int per_group = sc.group * sc.nqt;
+  const int grp = idx / per_group, in = idx - grp * per_group;
+  const int gh = min(sc.group, sc.heads - grp * sc.group);
+  const int r = in / gh, h = in - r * gh;
+  bh = (grp * sc.group + h) * sc.parts + part;
+  qt = causal ? sc.nqt - 1 - r : r;
+}
 
 // Item k of workgroup g: returns 1 and sets (bh, qt, split), 0 when the
 // workgroup has no item k (nor any later one), -1 for an empty slot (the
@@ -571,7 +611,7 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int BH,
     int H, int N, float scale_log2, AttnOptions opt, Schedule sched, int splits,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
+    float* __restrict__ o_part, float* __restrict__ lse_part, unsigned* __restrict__ queue) {
   using T = Tile<D>;
   constexpr int kDC = D / 16;
   constexpr int kDB = D / 32;
@@ -608,13 +648,38 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
     voff[i] = VCopy::template lane_offset<T::v_swz>(wave, lane, i);
   WaveState<D> st;
 
+  // kQueue (4-wavefront launches without bias or splits): thread 0 claims
+  // the items and hands each index to the workgroup through LDS (two slots,
+  // one per item parity).
+  constexpr bool kMayQueue = kW == 4 && !kBias && !kSplit;
+  const bool queued = kMayQueue && sched.mode == kQueue;
+  __shared__ int s_item[2];
+  const int part = (queued && sched.parts == 8) ? (blockIdx.x & 7) : 0;
+  int qidx = 0;
+  if (queued) {
+    if (tid == 0) s_item[0] = (int)atomicAdd(queue + part, 1u);
+    __syncthreads();
+    qidx = __builtin_amdgcn_readfirstlane(s_item[0]);
+  }
+
   for (int item = 0;; ++item) {
-    int bh, qt, split;
-    const int have = item_of(sched, blockIdx.x, item, BH, splits, kCausal, bh, qt, split);
-    if (have == 0) break;
-    if (have < 0) continue;
-    // Every wave is done with the LDS slots of the previous item.
-    if (item > 0) __syncthreads();
+    int bh, qt, split = 0;
+    unsigned next = 0;
+    // kQueue: the next item is claimed at the first of the last tiles, late
+    // enough that the claims follow the order in which workgroups become
+    // free, early enough that the atomic's round trip hides behind a tile.
+    bool claim = false;
+    if (queued) {
+      if (qidx >= sched.total) break;
+      queue_item(sched, qidx, part, kCausal, bh, qt);
+      claim = true;
+    } else {
+      const int have = item_of(sched, blockIdx.x, item, BH, splits, kCausal, bh, qt, split);
+      if (have == 0) break;
+      if (have < 0) continue;
+      // Every wave is done with the LDS slots of the previous item.
+      if (item > 0) __syncthreads();
+    }
 
     const int64_t head_off = (int64_t)bh * N * D;
     const uint16_t* kh = k + head_off;
@@ -689,7 +754,10 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
     if (sw_last >= s0) st.sc = sub_scores<D>((j_begin & 1) ? ks2 : ks0, off, st.qreg);
 
     int full_end = min(j_end, kvlen / kBN);
-    if constexpr (kCausal) full_end = min(full_end, q0 / kBN);
+    // Causal: tiles below this wave's first row are unmasked for it (other
+    // waves of the workgroup may mask them).
+    if constexpr (kCausal) full_end = min(full_end, qw / kBN);
+    if (sw_last < 0) full_end = j_begin;
     const int main_end = max(j_begin, min(full_end, j_end - 1));
     if constexpr (!kBias) {
       // When the item starts with an unmasked tile, its first sub-tile's row
@@ -726,9 +794,11 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
   auto cp1 = [&](int i) {                                                                     \
     if (i < VCopy::kPerWave) copy_v(ODD ? vb0 : vb1, (J) + 1, i);                             \
   }
-    // Main part: tiles that no wave masks (keys below the item's first query
+    // Main part: tiles this wave does not mask (keys below its first query
     // row when causal, whole tiles below the key length) and whose sub-tiles
-    // are all followed by another for every wave: one code path.
+    // are all followed by another: one code path.  The waves of a workgroup
+    // may run different numbers of main tiles; every tile, main or not, has
+    // its one barrier.
 #define OSM_MAIN_TILE(J, ODD)                                                                 \
   do {                                                                                        \
     __builtin_amdgcn_s_waitcnt(0);                                                            \
@@ -755,6 +825,10 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
   do {                                                                                        \
     __builtin_amdgcn_s_waitcnt(0);                                                            \
     __syncthreads();                                                                          \
+    if (claim) {                                                                              \
+      claim = false;                                                                          \
+      if (tid == 0) next = atomicAdd(queue + part, 1u);                                       \
+    }                                                                                         \
     OSM_TILE_COPIES(J, ODD);                                                                  \
     sub_step<D, kCausal, 0, true, true, kBias>(st, ODD ? ks3 : ks1, ODD ? vb1 : vb0, off,     \
                                                2 * (J), N, kvlen, qrow, half, scale_log2,     \
@@ -767,6 +841,10 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
   do {                                                                                        \
     __builtin_amdgcn_s_waitcnt(0);                                                            \
     __syncthreads();                                                                          \
+    if (claim) {                                                                              \
+      claim = false;                                                                          \
+      if (tid == 0) next = atomicAdd(queue + part, 1u);                                       \
+    }                                                                                         \
     OSM_TILE_COPIES(J, ODD);                                                                  \
     sub_step<D, kCausal, 0, true, true, kBias>(st, ODD ? ks3 : ks1, ODD ? vb1 : vb0, off,     \
                                                2 * (J), N, kvlen, qrow, half, scale_log2,     \
@@ -777,6 +855,10 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
   do {                                                                                        \
     __builtin_amdgcn_s_waitcnt(0);                                                            \
     __syncthreads();                                                                          \
+    if (claim) {                                                                              \
+      claim = false;                                                                          \
+      if (tid == 0) next = atomicAdd(queue + part, 1u);                                       \
+    }                                                                                         \
     OSM_TILE_COPIES(J, ODD);                                                                  \
     _Pragma("unroll") for (int i = 0; i < kDC - 1; ++i) {                                     \
       cp0(i);                                                                                 \
@@ -875,6 +957,21 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
         if (half == 0) lse[(int64_t)bh * N + qrow] = lse_val;
       }
     }
+    if (queued) {
+      // Hand over the next index; the barrier also tells every wave that the
+      // others are done with this item's LDS slots.
+      if (tid == 0) s_item[(item + 1) & 1] = (int)next;
+      __syncthreads();
+      qidx = __builtin_amdgcn_readfirstlane(s_item[(item + 1) & 1]);
+    }
+  }
+  if (queued && tid == 0) {
+    // Every workgroup of the partition has made its last claim once the exit
+    // counter reaches `workers`: the last one resets the slot.
+    if (atomicAdd(queue + 8 + part, 1u) == (unsigned)sched.workers - 1) {
+      queue[part] = 0u;
+      queue[8 + part] = 0u;
+    }
   }
 }
 
@@ -932,6 +1029,29 @@ int device_cus() {
   return n;
 }
 
+// The queue slot of the next persistent launch on the current device (the
+// array's address is looked up once per device).
+hipError_t queue_slot(unsigned** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex lock;
+  static unsigned* addr[kMaxDevices] = {};
+  static unsigned seq[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> guard(lock);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(fwd_queue));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<unsigned*>(p);
+  }
+  *ptr = addr[dev] + (seq[dev]++ % kQueueSlots) * 16;
+  return hipSuccess;
+}
+
 template <int D, int kW, bool kCausal, bool kBias, bool kSplit>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int H,
                   int N, float scale, const AttnOptions& opt, int splits, float* o_part,
@@ -943,6 +1063,11 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   sc.nqt = nqt;
   sc.pairs = (nqt + 1) / 2;
   sc.heads_per_xcd = BH / 8;
+  sc.parts = 1;
+  sc.heads = 0;
+  sc.group = 8;
+  sc.total = 0;
+  unsigned* queue = nullptr;
   int64_t grid;
   if (kSplit) {
     sc.mode = kOnePerGroup;
@@ -959,6 +1084,16 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
       sc.mode = kOnePerGroup;
       sc.workers = 0;
       grid = items;
+    } else if (kW == 4 && !kBias && slots >= 8) {
+      sc.mode = kQueue;
+      sc.parts = (BH & 7) == 0 ? 8 : 1;
+      sc.heads = BH / sc.parts;
+      sc.total = sc.heads * nqt;
+      const int per_part = slots / sc.parts;
+      sc.workers = sc.total < per_part ? sc.total : per_part;
+      grid = (int64_t)sc.parts * sc.workers;
+      const hipError_t e = queue_slot(&queue);
+      if (e != hipSuccess) return e;
     } else if ((BH & 7) == 0 && slots >= 8) {
       sc.mode = kPairsXcd;
       const int64_t per_xcd = (int64_t)sc.heads_per_xcd * sc.pairs;
@@ -975,7 +1110,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
                      dim3(Sh::kThreads), 0, s, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<uint16_t*>(o), lse, BH, H, N, scale_log2, opt, sc, splits, o_part,
-                     lse_part);
+                     lse_part, queue);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !kSplit) return e;
   const int64_t rows = (int64_t)BH * N;

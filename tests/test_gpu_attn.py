@@ -85,10 +85,13 @@ def test_odd_shapes_full(B, H, N, D, causal):
 
 # Grids with more query tiles than resident workgroups (MI355X: 256 compute
 # units; 512 slots for 128-row tiles at D = 128, 768 at D = 64, 256 for the
-# 256-row tiles of 8 wavefronts) run the persistent schedule: query tiles
-# folded in pairs (p, n - 1 - p), the middle tile alone when n is odd, dealt
-# over the heads of an XCD when B * H is a multiple of 8, else over all heads.
-PAIR_GRIDS = [
+# 256-row tiles of 8 wavefronts) run a persistent schedule.  With 128-row
+# tiles (4 wavefronts) the workgroups claim tiles from a work queue
+# (tests/test_gpu_attn_queue.py repeats such launches); with 256-row tiles
+# query tiles are folded in pairs (p, n - 1 - p), the middle tile alone when
+# n is odd, dealt over the heads of an XCD when B * H is a multiple of 8,
+# else over all heads.
+PERSISTENT_GRIDS = [
     (8, 40, 1920, 128, True),   # heads per XCD, 15 tiles of 128 rows
     (4, 50, 1152, 64, True),    # heads per XCD, D = 64, 9 tiles
     (3, 67, 1152, 64, True),    # B * H = 201: all heads
@@ -98,9 +101,9 @@ PAIR_GRIDS = [
 ]
 
 
-@pytest.mark.parametrize("B,H,N,D,causal", PAIR_GRIDS)
-def test_pair_schedules_sampled(B, H, N, D, causal):
-    _announce("pairs", B, H, N, D, causal)
+@pytest.mark.parametrize("B,H,N,D,causal", PERSISTENT_GRIDS)
+def test_persistent_schedules_sampled(B, H, N, D, causal):
+    _announce("persistent", B, H, N, D, causal)
     q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=N + H, device="cuda")
     scale = float(np.float32(1 / math.sqrt(D)))
     o, lse = osm.attn_fwd(q, k, v, scale, causal)

@@ -1,0 +1,103 @@
+"""GPU tests of the attention forward's work queue.
+
+Launches with 128-row tiles (4 wavefronts) and more query tiles than resident
+workgroups hand out their items through atomic counters in one of 64 queue
+slots per GPU, each launch taking the next slot and the last workgroup of the
+launch resetting it.  These tests run such launches many times in a row (every
+slot used more than once), on two streams at once, with partitions of 8 and of
+all heads and with a partial last group of heads, and check every output
+bitwise against the first launch and sampled rows against the float64 oracle.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_06_amd as osm
+import osm_inputs
+from oracle import attention_head_ref
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    osm.load_library()
+
+
+def _announce(*what):
+    print("[case]", *what, flush=True)
+
+
+def _check_sampled(q, k, v, scale, causal, o, lse, seed):
+    B, H, N, _ = q.shape
+    rng = np.random.default_rng(seed)
+    rows = sorted(set(rng.choice(N, 64, replace=False).tolist()) | {0, 127, 128, N - 1})
+    for b, h in osm_inputs.sample_heads(B, H, 3, seed, must=[(0, 0), (B - 1, H - 1)]):
+        qh, kh, vh = (t[b, h].cpu().double().numpy() for t in (q, k, v))
+        O, L = attention_head_ref(qh, kh, vh, scale, causal, query_rows=rows)
+        eo = np.abs(o[b, h].cpu().double().numpy()[rows] - O).max()
+        el = np.abs(lse[b, h].cpu().double().numpy()[rows] - L).max()
+        assert eo <= O_TOL and el <= LSE_TOL, ((b, h), eo, el)
+
+
+# (B, H, N, D, causal): query tiles per launch against resident workgroups
+# (MI355X: 512 at D = 128, 768 at D = 64).
+QUEUE_GRIDS = [
+    (1, 40, 2048, 128, True),   # 640 tiles, partitions of 5 heads
+    (1, 37, 2048, 128, True),   # 592 tiles, B * H = 37: one partition of all heads
+    (2, 48, 2048, 128, True),   # 12 heads per partition: groups of 8 and 4
+    (1, 64, 2048, 64, True),    # 1024 tiles, three workgroups per CU
+    (2, 48, 2048, 64, False),   # unmasked, equal items
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,causal", QUEUE_GRIDS)
+def test_queue_repeated_launches(B, H, N, D, causal):
+    _announce("queue repeated", B, H, N, D, causal)
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=B * 100 + H + D, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    o0, l0 = osm.attn_fwd(q, k, v, scale, causal)
+    o = torch.empty_like(o0)
+    lse = torch.empty_like(l0)
+    bad = torch.zeros((), dtype=torch.int64, device="cuda")
+    # 70 launches: every one of the 64 slots is used, some twice.
+    for _ in range(70):
+        o.fill_(0.5)
+        lse.fill_(0.5)
+        osm.attn_fwd(q, k, v, scale, causal, out=o, lse=lse)
+        bad += (o != o0).sum() + (lse != l0).sum()
+    torch.cuda.synchronize()
+    assert bad.item() == 0, f"{bad.item()} values differ from the first launch"
+    _check_sampled(q, k, v, scale, causal, o0, l0, seed=N + H)
+
+
+def test_queue_two_streams():
+    # Launches on two streams may run at the same time; each takes its own
+    # slot.  Every output must equal the one of a launch run alone.
+    B, H, N, D = 1, 40, 2048, 128
+    _announce("queue two streams", B, H, N, D)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    ins = [osm_inputs.attention_inputs(B, H, N, D, seed=s, device="cuda") for s in (3, 4)]
+    refs = [osm.attn_fwd(q, k, v, scale, True) for q, k, v in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty_like(refs[i][0]) for _ in range(12)] for i in range(2)]
+    lses = [[torch.empty_like(refs[i][1]) for _ in range(12)] for i in range(2)]
+    for r in range(12):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                q, k, v = ins[i]
+                osm.attn_fwd(q, k, v, scale, True, out=outs[i][r], lse=lses[i][r])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r in range(12):
+            assert torch.equal(outs[i][r], refs[i][0]) and torch.equal(lses[i][r], refs[i][1]), \
+                (i, r)
