@@ -130,9 +130,11 @@ struct Tile {
 // (row-major, 16-byte units XOR-swizzled by `Swz`), one instruction at a
 // time: instruction i of wave w fills LDS units [(w * kPerWave + i) * 64,
 // +64), one 16-byte unit per lane at a loop-invariant per-lane offset.  The
-// buffer descriptor starts at row k0 and ends with the head, so rows at or
-// past the end of the head fall outside its range and arrive as zeros; k0 =
-// N turns an instruction into a zero fill without memory traffic.
+// buffer descriptor (one per item) spans the head, so rows at or past the end
+// of the head fall outside its range and arrive as zeros; k0 = N turns an
+// instruction into a zero fill without memory traffic.  The row offset goes
+// into the lane offset (one vector add) rather than into a new descriptor
+// per copy, which took a dozen scalar instructions per copy.
 template <int D, int kRows, int kW>
 struct RowCopy {
   static constexpr int kUnits = D / 8;
@@ -144,16 +146,13 @@ struct RowCopy {
     const int row = p / kUnits, pu = p % kUnits;
     return row * (D * 2) + ((pu ^ Swz(row)) << 4);
   }
-  __device__ static void issue(char* buf, const uint16_t* base, int head_bytes, int k0, int wave,
-                               int i, int voff) {
+  template <typename Rsrc>
+  __device__ static void issue(char* buf, Rsrc head, int k0, int wave, int i, int voff) {
     // The buffer-to-LDS builtins exist only for the device; the host pass of
     // this single-source file sees an empty body.
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int left = head_bytes - k0 * (D * 2);
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)k0 * D), 0,
-                                                        left > 0 ? left : 0, kBufferFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, OSM_LDS(buf + (wave * kPerWave + i) * 1024), 16,
-                                             voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(head, OSM_LDS(buf + (wave * kPerWave + i) * 1024), 16,
+                                             voff + k0 * (D * 2), 0, 0, 0);
 #endif
   }
 };
@@ -712,11 +711,17 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
 
     // Copies of 32-row K sub-tiles and 64-row V tiles; a sub-tile or tile
     // outside this item's range becomes a zero fill (k0 = N).
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kh, 0, head_bytes, kBufferFlags);
+    const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vh, 0, head_bytes, kBufferFlags);
+#else
+    const int krsrc = 0, vrsrc = 0;
+#endif
     auto copy_k = [&](char* slot, int t, int i) {
-      KCopy::issue(slot, kh, head_bytes, t < s_end ? t * 32 : N, wave, i, koff[i]);
+      KCopy::issue(slot, krsrc, t < s_end ? t * 32 : N, wave, i, koff[i]);
     };
     auto copy_v = [&](char* buf, int jj, int i) {
-      VCopy::issue(buf, vh, head_bytes, jj < j_end ? jj * kBN : N, wave, i, voff[i]);
+      VCopy::issue(buf, vrsrc, jj < j_end ? jj * kBN : N, wave, i, voff[i]);
     };
 
     // A2 prologue: the first three K sub-tiles and the first V tile in flight.
