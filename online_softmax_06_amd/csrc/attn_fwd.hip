@@ -626,6 +626,13 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
   __shared__ __attribute__((aligned(1024))) char ks3[kSlot];
   __shared__ __attribute__((aligned(1024))) char vb0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char vb1[T::kBytes];
+  // Q staging (D = 128, 4 wavefronts, no splits): every wave's 32 query
+  // rows pass through LDS; waves 0-2 use the V buffer and the K slot that
+  // the prologue leaves free, wave 3 this array.  (With 8 wavefronts, at
+  // D = 64 and in the split kernels, measured level or slower, or spilling.)
+  constexpr bool kQLds = D == 128 && kW == 4 && !kSplit;
+  constexpr int kQStage = 32 * D * 2;
+  __shared__ __attribute__((aligned(256))) char qx[kQLds ? kQStage : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -742,11 +749,31 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
       if ((j_begin & 1) == 0) copy_v(vb0, j_begin, i); else copy_v(vb1, j_begin, i);
     }
 
-    // A1: this lane's part of Q as the B operand of S^T = K Q^T.
-    const uint16_t* qg = q + head_off + (int64_t)qrow * D + half * 8;
+    // A1: this lane's part of Q as the B operand of S^T = K Q^T.  Loaded
+    // directly, each instruction touches 32 rows in 32-byte pieces; with
+    // kQLds the wave copies its rows into LDS like a K sub-tile (whole
+    // 128-byte lines per instruction, the K swizzle) and reads them back in
+    // the operand layout after the barrier.  Rows past N arrive as zeros.
+    char* qst = qx;
+    if constexpr (kQLds) {
+      if (wave < 2) qst = ((j_begin & 1) ? vb0 : vb1) + wave * kQStage;
+      else if (wave == 2) qst = (j_begin & 1) ? ks1 : ks3;
+#if defined(__HIP_DEVICE_COMPILE__)
+      const auto qrsrc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(q + head_off), 0, head_bytes, kBufferFlags);
 #pragma unroll
-    for (int c = 0; c < kDC; ++c) {
-      st.qreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(qg + c * 16) : bf16x8{};
+      for (int i = 0; i < 32 * T::kUnits / 64; ++i) {
+        const int row = (i * 64 + lane) / T::kUnits, pu = (i * 64 + lane) % T::kUnits;
+        const int vo = (qw + row) * (D * 2) + ((pu ^ T::k_swz(row)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, OSM_LDS(qst + i * 1024), 16, vo, 0, 0, 0);
+      }
+#endif
+    } else {
+      const uint16_t* qg = q + head_off + (int64_t)qrow * D + half * 8;
+#pragma unroll
+      for (int c = 0; c < kDC; ++c) {
+        st.qreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(qg + c * 16) : bf16x8{};
+      }
     }
 #pragma unroll
     for (int i = 0; i < kDB; ++i) st.oacc[i] = f32x16{};
@@ -756,6 +783,15 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if constexpr (kQLds) {
+      // The staging slots are next written by the copies of the first tile,
+      // issued after its barrier, which every wave reaches only once these
+      // reads have completed.
+#pragma unroll
+      for (int c = 0; c < kDC; ++c) {
+        st.qreg[c] = *reinterpret_cast<const bf16x8*>(qst + (off.k ^ (c << 5)));
+      }
+    }
     if (sw_last >= s0) st.sc = sub_scores<D>((j_begin & 1) ? ks2 : ks0, off, st.qreg);
 
     int full_end = min(j_end, kvlen / kBN);
