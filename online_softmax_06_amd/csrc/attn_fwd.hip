@@ -1000,7 +1000,9 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
     }
     if (queued) {
       // Hand over the next index; the barrier also tells every wave that the
-      // others are done with this item's LDS slots.
+      // others are done with this item's LDS slots.  An item without key
+      // tiles (a batch whose key length is 0) has made no claim yet.
+      if (claim && tid == 0) next = atomicAdd(queue + part, 1u);
       if (tid == 0) s_item[(item + 1) & 1] = (int)next;
       __syncthreads();
       qidx = __builtin_amdgcn_readfirstlane(s_item[(item + 1) & 1]);

@@ -5,8 +5,9 @@ workgroups hand out their items through atomic counters in one of 64 queue
 slots per GPU, each launch taking the next slot and the last workgroup of the
 launch resetting it.  These tests run such launches many times in a row (every
 slot used more than once), on two streams at once, with partitions of 8 and of
-all heads and with a partial last group of heads, and check every output
-bitwise against the first launch and sampled rows against the float64 oracle.
+all heads, with a partial last group of heads and with key lengths (a batch
+without keys gives items without key tiles), and check every output bitwise
+against the first launch and sampled rows against the float64 oracle.
 """
 
 import math
@@ -101,3 +102,34 @@ def test_queue_two_streams():
         for r in range(12):
             assert torch.equal(outs[i][r], refs[i][0]) and torch.equal(lses[i][r], refs[i][1]), \
                 (i, r)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_queue_key_lengths(D):
+    # Key lengths make items of one query rank unequal, and a batch with no
+    # keys gives items without any key tile: they must still claim the next
+    # item (their rows get O = 0 and LSE = -inf).
+    B, H, N = 4, 48, 2048
+    _announce("queue key lengths", B, H, N, D)
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=61 + D, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    kv_len = torch.tensor([N, 0, 1000, 33], dtype=torch.int32, device="cuda")
+    o0, l0 = osm.attn_fwd(q, k, v, scale, True, kv_len=kv_len)
+    for _ in range(3):
+        o, lse = osm.attn_fwd(q, k, v, scale, True, kv_len=kv_len)
+        assert torch.equal(o, o0) and torch.equal(lse, l0)
+    torch.cuda.synchronize()
+    assert (o0[1] == 0).all() and torch.isinf(l0[1]).all() and (l0[1] < 0).all()
+    rng = np.random.default_rng(D)
+    rows = sorted(set(rng.choice(N, 48, replace=False).tolist()) | {0, 32, 33, 999, 1000, N - 1})
+    for b in range(B):
+        for h in (0, H - 1):
+            qh, kh, vh = (t[b, h].cpu().double().numpy() for t in (q, k, v))
+            O, L = attention_head_ref(qh, kh, vh, scale, True, query_rows=rows,
+                                      kv_len=int(kv_len[b]))
+            og = o0[b, h].cpu().double().numpy()[rows]
+            lg = l0[b, h].cpu().double().numpy()[rows]
+            assert np.abs(og - O).max() <= O_TOL, (b, h)
+            fin = np.isfinite(L)
+            assert (np.isinf(lg) == ~fin).all(), (b, h)
+            assert np.abs(lg[fin] - L[fin]).max(initial=0) <= LSE_TOL, (b, h)
