@@ -65,7 +65,12 @@ def test_queue_repeated_launches(B, H, N, D, causal):
     _announce("queue repeated", B, H, N, D, causal)
     q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=B * 100 + H + D, device="cuda")
     scale = float(np.float32(1 / math.sqrt(D)))
-    o0, l0 = osm.attn_fwd(q, k, v, scale, causal)
+    # Outputs start as NaN: a query tile that no workgroup claimed would keep it.
+    o0 = torch.full_like(q, float("nan"))
+    l0 = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    osm.attn_fwd(q, k, v, scale, causal, out=o0, lse=l0)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o0).any() and not torch.isnan(l0).any(), "unwritten rows"
     o = torch.empty_like(o0)
     lse = torch.empty_like(l0)
     bad = torch.zeros((), dtype=torch.int64, device="cuda")
