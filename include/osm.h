@@ -19,8 +19,9 @@
  *   - The attention forward hands out its work through 64 queue slots per
  *     GPU, one per launch in turn, each reset by the launch that used it: at
  *     most 64 forward launches may run at the same time on one GPU.  A
- *     launch captured in a HIP graph keeps its slot, so replays of one graph
- *     must not run concurrently with each other.
+ *     launch enqueued on a stream that is being captured into a HIP graph
+ *     uses no slot (it takes a fixed schedule), so graph replays may run
+ *     concurrently with each other and with eager launches.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
  *     the call returns without waiting.  The caller synchronises.
  *   - Arguments are validated on the host before any HIP call.  An invalid call

@@ -1095,6 +1095,21 @@ hipError_t queue_slot(unsigned** ptr) {
   return hipSuccess;
 }
 
+// Whether `s` is being captured into a graph.  A captured launch keeps its
+// kernel arguments, queue slot included, for every replay, while eager
+// launches go on taking the slots in turn: such a launch could meet another
+// on the same slot, so captured launches take a fixed schedule instead.
+// If the query itself fails, its error is cleared and the stream is taken
+// as captured.
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return st != hipStreamCaptureStatusNone;
+}
+
 template <int D, int kW, bool kCausal, bool kBias, bool kSplit>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int H,
                   int N, float scale, const AttnOptions& opt, int splits, float* o_part,
@@ -1127,7 +1142,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
       sc.mode = kOnePerGroup;
       sc.workers = 0;
       grid = items;
-    } else if (kW == 4 && !kBias && slots >= 8) {
+    } else if (kW == 4 && !kBias && slots >= 8 && !capturing(s)) {
       sc.mode = kQueue;
       sc.parts = (BH & 7) == 0 ? 8 : 1;
       sc.heads = BH / sc.parts;
