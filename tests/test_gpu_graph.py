@@ -98,3 +98,42 @@ def test_graph_replays_beside_eager_forward_launches():
                   "eager mismatches", bad_eager.item())
     assert bad_replay.item() == 0, f"{bad_replay.item()} values differ in graph replays"
     assert bad_eager.item() == 0, f"{bad_eager.item()} values differ in eager launches"
+
+
+# Captured launches of queue-sized grids (more query tiles than resident
+# workgroups: 512 at D = 128, 768 at D = 64) run the fixed pair schedules: all
+# heads dealt together when B * H is not a multiple of 8, per XCD otherwise.
+CAPTURE_GRIDS = [
+    (1, 37, 2048, 128, True),   # B * H = 37: pairs over all heads
+    (2, 48, 2048, 64, False),   # pairs per XCD, unmasked, D = 64
+    (2, 40, 2048, 64, True),    # pairs per XCD, causal, D = 64
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,causal", CAPTURE_GRIDS)
+def test_captured_forward_equals_eager(B, H, N, D, causal):
+    _announce("captured forward", B, H, N, D, causal)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=B * 10 + H + D, device="cuda")
+    o_ref, l_ref = osm.attn_fwd(q, k, v, scale, causal)
+    torch.cuda.synchronize()
+    o = torch.empty_like(q)
+    lse = torch.empty_like(l_ref)
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        osm.attn_fwd(q, k, v, scale, causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        osm.attn_fwd(q, k, v, scale, causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    for r in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), r
+        # Eager work between replays.
+        osm.attn_fwd(q, k, v, scale, causal)
+        torch.cuda.synchronize()
