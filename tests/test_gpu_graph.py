@@ -137,3 +137,46 @@ def test_captured_forward_equals_eager(B, H, N, D, causal):
         # Eager work between replays.
         osm.attn_fwd(q, k, v, scale, causal)
         torch.cuda.synchronize()
+
+
+def test_captured_split_and_masked_entry_points():
+    # The split entry points take their workspace from the caller (here
+    # torch's graph pool); masks, row lengths, key lengths and a bias are
+    # plain inputs.  Every replay must equal the eager launch bitwise.
+    B, H, N, D = 2, 4, 1536, 128
+    _announce("captured split/masked", B, H, N, D)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=81, device="cuda")
+    kv = torch.tensor([N, 1000], dtype=torch.int32, device="cuda")
+    g0 = torch.Generator(device="cuda").manual_seed(82)
+    bias = torch.randn((1, H, N, N), generator=g0, device="cuda")
+    x = osm_inputs.softmax_rows(64, 20000, seed=83, device="cuda")
+    mask = torch.randn((1, 20000), generator=g0, device="cuda")
+    rl = torch.randint(0, 20001, (64,), generator=g0, device="cuda", dtype=torch.int32)
+
+    def run():
+        a = osm.attn_fwd(q, k, v, scale, True, kv_len=kv, splits=4)
+        b = osm.attn_fwd(q, k, v, scale, False, bias=bias)
+        c = osm.softmax_rows(x, mask=mask, row_len=rl, split=True)
+        return (*a, *b, c)
+
+    refs = [t.clone() for t in run()]
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        outs = run()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, ref) in enumerate(zip(outs, refs)):
+            assert torch.equal(t, ref), (r, i)
+        run()  # eager work between replays
+        torch.cuda.synchronize()
