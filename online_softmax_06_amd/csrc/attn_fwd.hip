@@ -529,9 +529,10 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
 //                 finished its last items alone, one wavefront per SIMD, for
 //                 about a fifth of the launch.  Claiming lets the faster one
 //                 take more items.  Used for 4-wavefront launches without a
-//                 bias; with one 8-wavefront workgroup per CU kPairsXcd keeps
-//                 fewer heads in flight per L2 and is faster, and so it is
-//                 with a bias (whose score tiles the pairs also share).
+//                 bias, except those captured into a graph; with one
+//                 8-wavefront workgroup per CU kPairsXcd keeps fewer heads in
+//                 flight per L2 and is faster, and so it is with a bias (whose
+//                 score tiles the pairs also share).
 enum : int { kOnePerGroup = 0, kPairsXcd = 1, kPairsAll = 2, kQueue = 3 };
 
 struct Schedule {
