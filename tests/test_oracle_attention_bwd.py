@@ -3,7 +3,9 @@
 Central finite differences of the forward oracle (itself pinned in
 test_oracle_attention.py), torch's float64 CPU autograd of
 scaled_dot_product_attention, closed forms (one visible key, causal row 0) and
-three identities that every correct gradient of attention obeys.
+three identities that every correct gradient of attention obeys; the
+probabilities the gradients are built from, entry by entry from their
+definition.
 """
 
 import math
@@ -13,7 +15,7 @@ import pytest
 import torch
 
 from oracle import (attention_bwd_head_ref, attention_bwd_ref, attention_dq_rows_ref,
-                    attention_head_ref)
+                    attention_head_ref, attention_probs_head_ref)
 
 
 def _rand(shape, seed, sigma=1.0):
@@ -23,6 +25,30 @@ def _rand(shape, seed, sigma=1.0):
 def _loss(q, k, v, do, scale, causal, kv_len=None, bias=None):
     O, _ = attention_head_ref(q, k, v, scale, causal, kv_len=kv_len, bias=bias)
     return float(np.sum(O * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kv_len", [None, 3, 0])
+def test_probabilities_brute_force(causal, kv_len):
+    # P from its definition, one entry at a time in pure Python: e^s over the
+    # sum of e^s of the row's visible keys (causal: key <= row; key < kv_len;
+    # bias -inf hides a key); a row with no visible key is all zero.
+    n, d = 5, 3
+    q, k = _rand((n, d), 21), _rand((n, d), 22)
+    bias = _rand((n, n), 23)
+    bias[2, 1] = -np.inf
+    scale = 0.625  # a float32 value: the oracle takes the scale as float32
+    P = attention_probs_head_ref(q, k, scale, causal, kv_len=kv_len, bias=bias)
+    for i in range(n):
+        vis = [j for j in range(n)
+               if (not causal or j <= i) and (kv_len is None or j < kv_len)
+               and bias[i, j] != -np.inf]
+        e = {j: math.exp(scale * sum(q[i, t] * k[j, t] for t in range(d)) + bias[i, j])
+             for j in vis}
+        tot = sum(e.values())
+        for j in range(n):
+            want = e[j] / tot if j in e else 0.0
+            assert abs(P[i, j] - want) <= 1e-14, (i, j, P[i, j], want)
 
 
 @pytest.mark.parametrize("causal", [False, True])
