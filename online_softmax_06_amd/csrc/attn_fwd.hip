@@ -33,16 +33,15 @@
 // Exponent reference.  In exact arithmetic the result does not depend on the
 // reference m used in P = 2^(S' - m): the combine of §6.4.1 holds for any
 // finite one, and the pages' recurrence (m = the running max) is one choice.
-// Here the masked sub-tiles at the end of a row compute the row max first and
-// raise the reference only when the max exceeds it by more than kLag (log2
-// units).  The unmasked sub-tiles compute no max at all: P is formed against
-// the current reference and summed, and only when a lane's partial sum
-// leaves [0, 2^64] (a score far above the reference) or a row has no finite
-// reference yet does the wavefront take the max, raise the reference, rescale
-// O and l and form P again.  P <= 2^64 keeps every float32 sum and product in
-// range and bfloat16 P loses no precision; alpha is 1 on almost every
-// sub-tile, so the O rescale is skipped whenever it is 1 for the whole
-// wavefront.
+// Here no sub-tile computes a max as a rule: P is formed against the current
+// reference (the row max of the item's first unmasked sub-tile) and summed,
+// and only when a lane's partial sum leaves [0, 2^64] (a score far above the
+// reference) or a row has no finite reference yet does the wavefront take
+// the max, raise the reference (only when the max exceeds it by more than
+// kLag, in log2 units), rescale O and l and form P again.  P <= 2^64 keeps
+// every float32 sum and product in range and bfloat16 P loses no precision;
+// the rescale is rare, and masked sub-tiles differ only by hiding keys
+// (-inf) before their exponentials.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -283,16 +282,15 @@ struct WaveState {
 
 // One 32-key sub-tile s (keys [32 s, 32 s + 32), the half kKb of its 64-key
 // tile) for one wavefront, in two phases.
-//   Phase 1: the vector unit exponentiates the current scores and sums them;
-//            on unmasked sub-tiles the scores of sub-tile s + 1 (with kNext)
-//            are formed on the matrix core from `kslot_next` at the same
-//            time (neither depends on the other, so both units work side by
-//            side); masked sub-tiles first hide keys and take the row max.
-//   Phase 2: O is rescaled by alpha (only when some lane needs it), then
-//            O^T += V^T P^T on the two 16-key slices of this sub-tile, fed by
-//            transposed V reads from `vtile`, while the vector unit packs P to
-//            bfloat16; on masked sub-tiles the next scores are formed here,
-//            beside the PV products.
+//   Phase 1: the vector unit exponentiates the current scores (on masked
+//            sub-tiles, kMask, after hiding keys) and sums them, while the
+//            scores of sub-tile s + 1 (with kNext) are formed on the matrix
+//            core from `kslot_next` (neither depends on the other, so both
+//            units work side by side).  Rarely, O and the sums are then
+//            rescaled to a new exponent reference.
+//   Phase 2: O^T += V^T P^T on the two 16-key slices of this sub-tile, fed
+//            by transposed V reads from `vtile`, while the vector unit packs
+//            P to bfloat16.
 // Each phase is a sequence of short regions (one or two products, the LDS
 // reads they need two regions later, a share of the vector work) fenced by
 // sched_barrier, so the compiler keeps this interleaving.  `copy(i)` issues
@@ -335,85 +333,26 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
     va[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   f32x16 sn = f32x16{};
-  if constexpr (kNext && !kMask) {
+  if constexpr (kNext) {
     read_k(0);
     read_k(1);
   }
   float p[16];
   float alpha = 1.0f;
   float ps0 = 0.0f, ps1 = 0.0f;  // this lane's half of the sub-tile's row sum
-  if constexpr (kMask) {
-    // Masked sub-tiles (the last key tiles): the row max decides the new
-    // reference before any exponential.  Here the vector work of phase 1
-    // runs alone and the next scores are formed in phase 2, beside the PV
-    // products, once P is packed: with the float32 P, the next scores and
-    // their K operands all live at once, the extra registers of the masking
-    // push the kernel past 256 VGPRs.
-    float m_new = 0.0f, ref = 0.0f;
-    constexpr int kExpRegions = kDC - 1;
-#pragma unroll
-    for (int c = 0; c < kDC; ++c) {
-      // One global->LDS copy instruction per region (regions 1..): spread
-      // out, they do not queue up behind the other waves' copies.
-      if (c > 0) copy(c - 1);
-      if (c == 0) {
-        // A4: hide keys past the causal diagonal or past the valid keys.
-        // Score i is key k0 + (i / 4) * 8 + half * 4 + i % 4: visible when
-        // (i / 4) * 8 + i % 4 is below lim.
-        const int lim = (kCausal ? min(kvlen, qrow + 1) : kvlen) - k0 - half * 4;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = (i >> 2) * 8 + (i & 3) < lim ? sc[i] : kNegInf;
-        // A5: row max over this lane's 16 keys and its partner's 16, the new
-        // exponent reference (raised only past kLag) and alpha.
-        float mx = max3(sc[0], sc[1], sc[2]);
-#pragma unroll
-        for (int i = 3; i < 15; i += 2) mx = max3(mx, sc[i], sc[i + 1]);
-        mx = __builtin_fmaxf(mx, sc[15]);
-        mx = __builtin_fmaxf(mx, swap_halves(mx));
-        const float mt = mx * scale_log2;
-        m_new = mt > st.m_run + kLag ? mt : st.m_run;
-        ref = finite_ref(m_new);
-        alpha = exp2_hw(st.m_run - ref);
-      } else {
-        // P = 2^(S * scale * log2 e - ref).
-        const int lo = (c - 1) * 16 / kExpRegions, hi = c * 16 / kExpRegions;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (i >= lo && i < hi) {
-            p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref));
-            if (i & 1) ps1 += p[i]; else ps0 += p[i];
-          }
-        }
-        asm volatile("" : "+v"(ps0), "+v"(ps1));
-      }
-      if (c == kDC - 1) {
-        read_v(0);
-        read_v(1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    st.m_run = m_new;
-    // Keep the exponentials in phase 1: without this use the compiler sinks
-    // them past the rescale branch, next to the products that consume them.
-    asm volatile("" ::"v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]),
-                 "v"(p[6]), "v"(p[7]), "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]),
-                 "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
-    // Rescale the accumulator, skipped when alpha is 1 on every lane.
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-      // The empty asm keeps this a branch: without it the compiler would
-      // multiply unconditionally, since scaling by 1 is harmless.
-      asm volatile("");
-#pragma unroll
-      for (int b = 0; b < kDB; ++b) st.oacc[b] *= alpha;
-    }
-  } else {
-    // Unmasked sub-tiles: no row max.  P is formed against the current
-    // reference right away and summed; the reference moves only when a
-    // lane's partial sum leaves [0, 2^64] (a score far above the reference:
-    // too large for the sums, or +inf) or a row has no finite reference yet
-    // (its first sub-tile).  Any finite reference gives the same result in
-    // exact arithmetic, and P <= 2^64 keeps every sum and product in range.
+  {
+    // No row max: P is formed against the current reference right away and
+    // summed; the reference moves only when a lane's partial sum leaves
+    // [0, 2^64] (a score far above the reference: too large for the sums, or
+    // +inf) or a row has no finite reference yet (its first visible keys).
+    // Any finite reference gives the same result in exact arithmetic, and
+    // P <= 2^64 keeps every sum and product in range.
     const float ref = finite_ref(st.m_run);
+    // A4 (masked sub-tiles, the last key tiles): score i is key k0 + (i / 4)
+    // * 8 + half * 4 + i % 4, hidden (-inf, so P = 0) unless (i / 4) * 8 +
+    // i % 4 is below lim; each region hides its scores before their
+    // exponentials.
+    const int lim = kMask ? (kCausal ? min(kvlen, qrow + 1) : kvlen) - k0 - half * 4 : 0;
     constexpr int kPer = 16 / kDC;  // exponentials per region
 #pragma unroll
     for (int c = 0; c < kDC; ++c) {
@@ -425,6 +364,7 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
 #pragma unroll
       for (int t = 0; t < kPer; ++t) {
         const int i = c * kPer + t;
+        if constexpr (kMask) sc[i] = (i >> 2) * 8 + (i & 3) < lim ? sc[i] : kNegInf;
         p[i] = exp2_hw(__builtin_fmaf(sc[i], scale_log2, -ref));
         // The sums start as p0 + p2 and p1 + p3: no add of 0 and no copy.
         if (i == 2) ps0 = p[0] + p[2];
@@ -474,7 +414,7 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
     }
   }
 
-  // Phase 2 (A6): O^T += V^T P^T (and, on masked sub-tiles, the next scores).
+  // Phase 2 (A6): O^T += V^T P^T.
   // P in the B-operand layout: slice kc2 holds scores kc2 * 8 + 0..7, i.e.
   // keys 16 kc2 + {0..3, 8..11} + 4 half, the order the V reads follow.
   bf16x8 pb[2];
@@ -485,21 +425,12 @@ __device__ __forceinline__ void sub_step(WaveState<D>& st, const char* kslot_nex
                            pack_bf16x2(p[o + 4], p[o + 5]), pack_bf16x2(p[o + 6], p[o + 7])));
   };
   pack_p(0);
-  static_assert(kPV == kDC, "one next-score product per PV product");
-  if constexpr (kMask && kNext) {
-    read_k(0);
-    read_k(1);
-  }
 #pragma unroll
   for (int i = 0; i < kPV; ++i) {
     const int kc2 = i / kDB, b = i % kDB;
     if (i + 2 < kPV) read_v(i + 2);
     if (i == 0) pack_p(1);
     st.oacc[b] = mfma32(va[i % 3], pb[kc2], st.oacc[b]);
-    if constexpr (kMask && kNext) {
-      if (i + 2 < kDC) read_k(i + 2);
-      sn = mfma32(ka[i % 3], st.qreg[i], sn);
-    }
     __builtin_amdgcn_sched_barrier(0);
   }
   st.l_run = st.l_run * alpha + (ps0 + ps1);
