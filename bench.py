@@ -11,8 +11,9 @@ launches, reported in ``rooflines`` with ``"in_step": false``):
   4. attention backward (dQ, dK, dV from the forward's O and LSE) on the same
      layer, also under ``attention_backward``;
   5. the long-context causal forward, B=1 H=32 N=16384 D=128;
-  6. the small non-causal forward, B=1 H=8 N=1024 D=64 (64 query tiles for
-     256 compute units and a cache-resident working set: latency-bound);
+  6. the small non-causal forward, B=1 H=8 N=1024 D=64 (256 workgroups of
+     32 query rows whose wavefronts split the keys, on a cache-resident
+     working set: latency-bound);
   7. the small softmax workload, its three calls (62 x 1000, 2 x 100, 1 x 3),
      a latency figure per call;
   8. ``osm_stream_copy`` of the float32 softmax bytes (1 GiB read + 1 GiB
@@ -172,8 +173,9 @@ def make_units(torch, osm, osm_inputs, only):
                                "attn_fwd_kernel<128, causal> (8 wavefronts)", False))
     if want("attn_small"):
         units.append(attn_unit(
-            torch, osm, osm_inputs, "attn_small", "attn_fwd_kernel<64, non-causal>", False,
-            note="latency-bound: 64 query tiles for 256 compute units, cache-resident inputs"))
+            torch, osm, osm_inputs, "attn_small", "attn_fwd_small_kernel<64, non-causal>", False,
+            note="latency-bound: 256 workgroups of 32 query rows, keys split over their "
+                 "wavefronts, cache-resident inputs"))
     if want("softmax_small"):
         d = osm_inputs.softmax_small()
         calls = [(label, x.cuda(), torch.empty_like(x, device="cuda")) for label, x in d["calls"]]

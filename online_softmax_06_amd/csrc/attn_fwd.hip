@@ -4,7 +4,8 @@
 //
 // Method ("Ch.6 Softmax and Online Softmax" §6.5-§6.6; xxqk §4.1): a workgroup
 // owns a tile of 128 or 256 query rows and streams the key/value tiles of its
-// (batch, head) through LDS.  Per tile it forms the scores on the matrix
+// (batch, head) through LDS (grids too small to fill the GPU: 32 rows, the
+// keys split over the four wavefronts and their partial states combined).  Per tile it forms the scores on the matrix
 // cores, updates the running max m and rescaled sum l of every query row,
 // rescales the output accumulator by alpha = 2^(m_old - m_new), and adds
 // P V_j with P = 2^(S' - m_new) (S' = S * scale * log2 e), the form that needs
@@ -950,6 +951,157 @@ __global__ __launch_bounds__((Shape<D, kW>::kThreads),
   }
 }
 
+// Grids too small to fill the GPU (few heads and query tiles): a workgroup
+// owns only 32 query rows and its four wavefronts split their key range
+// into four consecutive parts.  Every wavefront streams its own part through
+// LDS areas of its own (no barrier inside the key loop), each sub-tile
+// handled by the masked sub-step (keys past the causal diagonal or the key
+// length hidden), and ends with a partial state (reference, sum, O) of the
+// same rows.  Wavefronts 1-3 leave theirs in LDS and wavefront 0 folds the
+// four in order with the (m, l) combine of §6.4.1 before the epilogue.
+// Four times the workgroups of the 128-row kernel, each with a quarter of
+// the key loop.
+template <int D, bool kCausal>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_fwd_small_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int BH,
+    int H, int N, float scale_log2, AttnOptions opt) {
+  using T = Tile<D>;
+  using SubCopy = RowCopy<D, 32, 1>;  // one wavefront copies a 32-row sub-tile
+  constexpr int kDC = D / 16, kDB = D / 32;
+  constexpr int kSub = 32 * D * 2;  // bytes of a 32-row sub-tile
+  // Per wavefront: two K and two V sub-tile slots (double buffering).
+  __shared__ __attribute__((aligned(1024))) char area[4][4][kSub];
+  static_assert(kDB * 16 * 64 * 4 + 2 * 64 * 4 <= 4 * kSub, "partial state fits the area");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int ngroups = (N + 31) / 32;
+  const int bh = blockIdx.x / ngroups;
+  const int q0 = (blockIdx.x % ngroups) * 32;
+  const int qrow = q0 + col;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const int head_bytes = N * D * 2;
+  const int kvlen = opt.kv_len ? min(max(opt.kv_len[bh / H], 0), N) : N;
+  const LaneOffsets<D> off = lane_offsets<D>(lane);
+
+  // This wavefront's sub-tiles [s_lo, s_hi) of the rows' visible keys.
+  const int kv_end = kCausal ? min(kvlen, q0 + 32) : kvlen;
+  const int nsub = (kv_end + 31) / 32;
+  const int per = (nsub + 3) / 4;
+  const int s_lo = min(wave * per, nsub), s_hi = min(s_lo + per, nsub);
+
+  WaveState<D> st;
+  {
+    const uint16_t* qg = q + head_off + (int64_t)qrow * D + half * 8;
+#pragma unroll
+    for (int c = 0; c < kDC; ++c)
+      st.qreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(qg + c * 16) : bf16x8{};
+  }
+#pragma unroll
+  for (int b = 0; b < kDB; ++b) st.oacc[b] = f32x16{};
+  st.m_run = kNegInf;
+  st.l_run = 0.0f;
+  st.sc = f32x16{};
+
+  char* const kslot[2] = {area[wave][0], area[wave][1]};
+  char* const vslot[2] = {area[wave][2], area[wave][3]};
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto krsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(k + head_off), 0, head_bytes, kBufferFlags);
+  const auto vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(v + head_off), 0, head_bytes, kBufferFlags);
+#else
+  const int krsrc = 0, vrsrc = 0;
+#endif
+  int koff[SubCopy::kPerWave], voff[SubCopy::kPerWave];
+#pragma unroll
+  for (int i = 0; i < SubCopy::kPerWave; ++i) {
+    koff[i] = SubCopy::template lane_offset<T::k_swz>(0, lane, i);
+    voff[i] = SubCopy::template lane_offset<T::v_swz>(0, lane, i);
+  }
+  // Rows past the head fall outside the descriptors and arrive as zeros.
+  auto copy_sub = [&](int slot, int s) {
+#pragma unroll
+    for (int i = 0; i < SubCopy::kPerWave; ++i) {
+      SubCopy::issue(kslot[slot], krsrc, s * 32, 0, i, koff[i]);
+      SubCopy::issue(vslot[slot], vrsrc, s * 32, 0, i, voff[i]);
+    }
+  };
+  auto no_copy = [](int) {};
+
+  if (s_lo < s_hi) copy_sub(0, s_lo);
+  for (int s = s_lo; s < s_hi; ++s) {
+    const int slot = (s - s_lo) & 1;
+    // This wavefront's copies of sub-tile s have landed in LDS; the other
+    // slot was last read by sub-tile s - 1, whose products have consumed it.
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+    if (s + 1 < s_hi) copy_sub(slot ^ 1, s + 1);
+    st.sc = sub_scores<D>(kslot[slot], off, st.qreg);
+    sub_step<D, kCausal, 0, false, true, false>(st, kslot[slot], vslot[slot], off, s, N, kvlen,
+                                                qrow, half, scale_log2, nullptr, opt, no_copy);
+  }
+
+  // Partial state of this wavefront's part: P was formed against
+  // ref = finite_ref(m_run), so the part's sum is l * 2^ref and its output O.
+  const float ref = finite_ref(st.m_run);
+  const float l_tot = st.l_run + swap_halves(st.l_run);
+  __syncthreads();  // every wavefront is done with its key loop
+  float* part = reinterpret_cast<float*>(area[wave][0]);
+  if (wave > 0) {
+#pragma unroll
+    for (int b = 0; b < kDB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part[(b * 16 + i) * 64 + lane] = st.oacc[b][i];
+    part[kDB * 16 * 64 + lane] = ref;
+    part[kDB * 16 * 64 + 64 + lane] = l_tot;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  // A7 after the combine, parts in order 0..3: M = the largest reference of
+  // the parts with keys, weights 2^(ref_w - M) <= 1.
+  float refs[4], ls[4];
+  refs[0] = ref;
+  ls[0] = l_tot;
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    const float* pw = reinterpret_cast<const float*>(area[w][0]);
+    refs[w] = pw[kDB * 16 * 64 + lane];
+    ls[w] = pw[kDB * 16 * 64 + 64 + lane];
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = ls[w] > 0.0f ? fmaxf(M, refs[w]) : M;
+  float wgt[4];
+  float l_all = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wgt[w] = ls[w] > 0.0f ? exp2_hw(refs[w] - M) : 0.0f;
+    l_all += wgt[w] * ls[w];
+  }
+#pragma unroll
+  for (int b = 0; b < kDB; ++b) {
+    st.oacc[b] *= wgt[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float* pw = reinterpret_cast<const float*>(area[w][0]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.oacc[b][i] += wgt[w] * pw[(b * 16 + i) * 64 + lane];
+    }
+  }
+  const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
+  if (qrow < N) {
+    uint16_t* orow = o + head_off + (int64_t)qrow * D;
+#pragma unroll
+    for (int b = 0; b < kDB; ++b) store_block_bf16(orow + b * 32, st.oacc[b], half, inv);
+    if (half == 0) lse[(int64_t)bh * N + qrow] = l_all > 0.0f ? (M + log2_hw(l_all)) * kLn2 : kNegInf;
+  }
+}
+
 // Merge the splits of every query row: with M = max_s LSE_s and
 // w_s = e^(LSE_s - M), LSE = M + log sum_s w_s and O = sum_s w_s O_s / sum_s w_s
 // -- the (m, l) combine of §6.4.1 written for normalised partial outputs.
@@ -1111,10 +1263,36 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   return hipGetLastError();
 }
 
+template <int D, bool kCausal>
+hipError_t launch_small(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                        int H, int N, float scale, const AttnOptions& opt, hipStream_t s) {
+  const int64_t grid = (int64_t)BH * ((N + 31) / 32);
+  hipLaunchKernelGGL((attn_fwd_small_kernel<D, kCausal>), dim3((unsigned)grid), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, H, N,
+                     scale * kLog2e, opt);
+  return hipGetLastError();
+}
+
 template <int D, bool kSplit>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                     int H, int N, float scale, bool causal, const AttnOptions& opt, int splits,
                     float* o_part, float* lse_part, hipStream_t s) {
+  if constexpr (!kSplit) {
+    // Grids whose 128-row query tiles would leave half the compute units
+    // idle: 32-row workgroups with the key range split over their
+    // wavefronts, up to 4096 keys at D = 64 and 1024 at D = 128.  Measured
+    // against the 128-row kernel: B1 H8 N1024 D64 30% faster, B1 H4 N4096 D64
+    // causal 22%, B1 H8 N1024 D128 13%; at D = 128 and 2048 keys or more it
+    // was 25-50% slower (each wavefront streams its own K/V, four times the
+    // L2 reads, and 128 KiB of LDS leave one wavefront per SIMD).
+    const int64_t tiles = (int64_t)BH * ((N + 127) / 128);
+    const bool short_rows = D == 64 ? N <= 4096 : N <= 1024;
+    if (opt.bias == nullptr && short_rows && 2 * tiles <= device_cus()) {
+      return causal ? launch_small<D, true>(q, k, v, o, lse, BH, H, N, scale, opt, s)
+                    : launch_small<D, false>(q, k, v, o, lse, BH, H, N, scale, opt, s);
+    }
+  }
   if (opt.bias != nullptr) {
     return causal ? launch<D, 4, true, true, kSplit>(q, k, v, o, lse, BH, H, N, scale, opt, splits,
                                                      o_part, lse_part, s)

@@ -290,3 +290,46 @@ def test_raw_abi_attention_small_config():
     torch.cuda.synchronize()
     eo, el = compare(q, k, v, cfg["scale"], cfg["causal"], o, lse)
     print(f"[result] raw osm_attn_fwd attn_small O err {eo:.3g} LSE err {el:.3g}", flush=True)
+
+
+# Small grids (128-row query tiles for at most half the compute units) run
+# 32-row workgroups whose four wavefronts split the key range and merge their
+# partial states: up to 4096 keys at D = 64, 1024 at D = 128.  Cases at the
+# limits, with wavefronts left without keys (N < 128) and with key lengths
+# (a batch without keys gives rows with O = 0 and LSE = -inf).
+SMALL_GRIDS = [
+    (1, 4, 4096, 64, True, None),
+    (1, 8, 1024, 128, True, None),
+    (1, 8, 1024, 128, False, None),
+    (2, 3, 77, 128, False, None),
+    (1, 2, 33, 64, True, None),
+    (2, 4, 1000, 64, True, [1000, 0]),
+    (2, 4, 700, 128, False, [513, 9]),
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,causal,kv", SMALL_GRIDS)
+def test_small_grid_key_split(B, H, N, D, causal, kv):
+    _announce("small grid", B, H, N, D, causal, kv)
+    q, k, v = osm_inputs.attention_inputs(B, H, N, D, seed=N + D + H, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(D)))
+    kv_len = None if kv is None else torch.tensor(kv, dtype=torch.int32, device="cuda")
+    o, lse = osm.attn_fwd(q, k, v, scale, causal, kv_len=kv_len)
+    o2, l2 = osm.attn_fwd(q, k, v, scale, causal, kv_len=kv_len)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2), "run-to-run difference"
+    og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    rng = np.random.default_rng(N)
+    rows = None if N <= 1024 else sorted(set(rng.choice(N, 256, replace=False).tolist())
+                                         | {0, 31, 32, 1023, 1024, N - 1})
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = (t[b, h].cpu().double().numpy() for t in (q, k, v))
+            O, L = attention_head_ref(qh, kh, vh, scale, causal, query_rows=rows,
+                                      kv_len=None if kv is None else kv[b])
+            ob = og[b, h] if rows is None else og[b, h][rows]
+            lb = lg[b, h] if rows is None else lg[b, h][rows]
+            dead = np.isneginf(L)
+            assert (np.isneginf(lb) == dead).all() and (ob[dead] == 0).all(), (b, h)
+            assert np.abs(ob - O).max() <= O_TOL, (b, h, np.abs(ob - O).max())
+            assert np.abs(lb[~dead] - L[~dead]).max(initial=0) <= LSE_TOL, (b, h)
