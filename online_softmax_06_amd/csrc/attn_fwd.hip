@@ -978,9 +978,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_fwd_small_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
+  // All 32-row groups of a head on one XCD when B * H is a multiple of 8
+  // (the L2 of that XCD then fetches the head's K and V once), causal groups
+  // heaviest first.
   const int ngroups = (N + 31) / 32;
-  const int bh = blockIdx.x / ngroups;
-  const int q0 = (blockIdx.x % ngroups) * 32;
+  int bh, grp;
+  tile_of(blockIdx.x, ngroups, BH, kCausal, bh, grp);
+  const int q0 = grp * 32;
   const int qrow = q0 + col;
   const int64_t head_off = (int64_t)bh * N * D;
   const int head_bytes = N * D * 2;
