@@ -1284,14 +1284,14 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float*
                     float* o_part, float* lse_part, hipStream_t s) {
   if constexpr (!kSplit) {
     // Grids whose 128-row query tiles would leave half the compute units
-    // idle: 32-row workgroups with the key range split over their
-    // wavefronts, up to 4096 keys at D = 64 and 1024 at D = 128.  Measured
-    // against the 128-row kernel: B1 H8 N1024 D64 30% faster, B1 H4 N4096 D64
-    // causal 22%, B1 H8 N1024 D128 13%; at D = 128 and 2048 keys or more it
-    // was 25-50% slower (each wavefront streams its own K/V, four times the
-    // L2 reads, and 128 KiB of LDS leave one wavefront per SIMD).
+    // idle (so B * H * N <= 16384 * 128): 32-row workgroups with the key
+    // range split over their wavefronts, at D = 64 always and at D = 128 up
+    // to 1024 keys.  Measured against the 128-row kernel: B1 H8 N1024 D64
+    // 30% faster, B1 H1 N16384 D64 causal 34%, B1 H8 N1024 D128 13%; at
+    // D = 128 with 2048 keys or more level to 50% slower (each wavefront
+    // streams its own K/V, and 128 KiB of LDS leave one wavefront per SIMD).
     const int64_t tiles = (int64_t)BH * ((N + 127) / 128);
-    const bool short_rows = D == 64 ? N <= 4096 : N <= 1024;
+    const bool short_rows = D == 64 || N <= 1024;
     if (opt.bias == nullptr && short_rows && 2 * tiles <= device_cus()) {
       return causal ? launch_small<D, true>(q, k, v, o, lse, BH, H, N, scale, opt, s)
                     : launch_small<D, false>(q, k, v, o, lse, BH, H, N, scale, opt, s);

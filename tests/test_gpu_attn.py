@@ -294,10 +294,11 @@ def test_raw_abi_attention_small_config():
 
 # Small grids (128-row query tiles for at most half the compute units) run
 # 32-row workgroups whose four wavefronts split the key range and merge their
-# partial states: up to 4096 keys at D = 64, 1024 at D = 128.  Cases at the
-# limits, with wavefronts left without keys (N < 128) and with key lengths
-# (a batch without keys gives rows with O = 0 and LSE = -inf).
+# partial states: at D = 64 for every such grid, at D = 128 up to 1024 keys.
+# Cases at the limits, with wavefronts left without keys (N < 128) and with
+# key lengths (a batch without keys gives rows with O = 0 and LSE = -inf).
 SMALL_GRIDS = [
+    (1, 1, 16384, 64, True, None),
     (1, 4, 4096, 64, True, None),
     (1, 8, 1024, 128, True, None),
     (1, 8, 1024, 128, False, None),
@@ -321,7 +322,7 @@ def test_small_grid_key_split(B, H, N, D, causal, kv):
     og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
     rng = np.random.default_rng(N)
     rows = None if N <= 1024 else sorted(set(rng.choice(N, 256, replace=False).tolist())
-                                         | {0, 31, 32, 1023, 1024, N - 1})
+                                         | {0, 31, 32, 1023, 1024, N // 2, N - 1})
     for b in range(B):
         for h in range(H):
             qh, kh, vh = (t[b, h].cpu().double().numpy() for t in (q, k, v))
