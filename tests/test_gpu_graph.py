@@ -142,7 +142,8 @@ def test_captured_forward_equals_eager(B, H, N, D, causal):
 def test_captured_split_and_masked_entry_points():
     # The split entry points take their workspace from the caller (here
     # torch's graph pool); masks, row lengths, key lengths and a bias are
-    # plain inputs.  Every replay must equal the eager launch bitwise.
+    # plain inputs; the small-grid forward keeps its partial states in LDS.
+    # Every replay must equal the eager launch bitwise.
     B, H, N, D = 2, 4, 1536, 128
     _announce("captured split/masked", B, H, N, D)
     scale = float(np.float32(1 / math.sqrt(D)))
@@ -153,12 +154,15 @@ def test_captured_split_and_masked_entry_points():
     x = osm_inputs.softmax_rows(64, 20000, seed=83, device="cuda")
     mask = torch.randn((1, 20000), generator=g0, device="cuda")
     rl = torch.randint(0, 20001, (64,), generator=g0, device="cuda", dtype=torch.int32)
+    # A small grid (B1 H8 N1024 D64): 32-row workgroups that split the keys.
+    qs, ks, vs = osm_inputs.attention_inputs(1, 8, 1024, 64, seed=84, device="cuda")
 
     def run():
         a = osm.attn_fwd(q, k, v, scale, True, kv_len=kv, splits=4)
         b = osm.attn_fwd(q, k, v, scale, False, bias=bias)
         c = osm.softmax_rows(x, mask=mask, row_len=rl, split=True)
-        return (*a, *b, c)
+        d = osm.attn_fwd(qs, ks, vs, 0.125, False)
+        return (*a, *b, c, *d)
 
     refs = [t.clone() for t in run()]
     torch.cuda.synchronize()
