@@ -294,10 +294,16 @@ def test_raw_abi_attention_small_config():
 
 # Small grids (128-row query tiles for at most half the compute units) run
 # 32-row workgroups whose four wavefronts split the key range and merge their
-# partial states: at D = 64 for every such grid, at D = 128 up to 1024 keys.
-# Cases at the limits, with wavefronts left without keys (N < 128) and with
-# key lengths (a batch without keys gives rows with O = 0 and LSE = -inf).
+# partial states: at D = 64 for every such grid, at D = 128 up to 1024 keys
+# (longer D = 128 rows keep the 128-row kernel, one workgroup per tile; the
+# first cases).  Cases at the limits, with wavefronts left without keys
+# (N < 128) and with key lengths (a batch without keys gives rows with O = 0
+# and LSE = -inf).
 SMALL_GRIDS = [
+    (1, 8, 2048, 128, True, None),
+    (1, 2, 4100, 128, False, None),
+    (2, 2, 1500, 128, True, [1500, 700]),
+    (1, 1, 16384, 128, True, None),
     (1, 1, 16384, 64, True, None),
     (1, 4, 4096, 64, True, None),
     (1, 8, 1024, 128, True, None),
